@@ -1,0 +1,363 @@
+// C-ABI front end of libfa.so: argument validation, launch planning (tiles,
+// key-split counts, workspace carving) and kernel launch. Every check runs on
+// the host before anything is enqueued.
+//
+// Planning follows two lessons of "CUDA: fix FA occupancy, optimize tile kernel"
+// (llama.cpp, opening paragraph): launch enough workgroups to occupy every
+// compute unit (the occupancy bug there launched too few), and size tiles to the
+// chip (here 160 KiB of LDS and 256 CUs of MI355X).
+#include <algorithm>
+#include <climits>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+
+#include "fa.h"
+#include "fa_kernels.h"
+
+using namespace fa;
+
+namespace {
+
+// Compute units the planner targets. gfx950 parts (MI350X / MI355X) have 256;
+// planning never queries the device, so workspace sizes are pure functions of
+// the shape. FA_NUM_CUS overrides it for experiments.
+int planner_cus() {
+  static int cus = [] {
+    const char* e = std::getenv("FA_NUM_CUS");
+    int v = e ? std::atoi(e) : 256;
+    return v > 0 ? v : 256;
+  }();
+  return cus;
+}
+
+int env_int(const char* name, int dflt) {
+  const char* e = std::getenv(name);
+  if (!e || !*e) return dflt;
+  return std::atoi(e);
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int ceil_div(int64_t a, int64_t b) { return (int)((a + b - 1) / b); }
+
+constexpr int64_t kMaxGrid = 0x7fffffff;
+
+// ---------------------------------------------------------------------------
+// prefill planning
+// ---------------------------------------------------------------------------
+struct PrefillPlan {
+  int n_qtiles = 0;
+  int n_splits = 1;
+  size_t ws_bytes = 0;
+};
+
+PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split) {
+  PrefillPlan pl;
+  pl.n_qtiles = ceil_div(Sq, PF_BM);
+  const int64_t base = (int64_t)B * Hq * pl.n_qtiles;
+  const int max_tiles = ceil_div(Skv, PF_BN);
+  int S = 1;
+  if (allow_split && base > 0) {
+    const int forced = env_int("FA_PREFILL_SPLITS", 0);
+    if (forced > 0) {
+      S = std::min(forced, 64);
+    } else {
+      // Two 4-wave workgroups per CU keep two waves on every SIMD; split the
+      // keys only while each split keeps at least 8 tiles (512 keys).
+      const int64_t target = 2 * (int64_t)planner_cus();
+      while (base * S < target && S < 16 && max_tiles / (2 * S) >= 8) S *= 2;
+    }
+    S = std::max(1, std::min(S, std::max(1, max_tiles)));
+  }
+  pl.n_splits = S;
+  if (S > 1) pl.ws_bytes = (size_t)S * B * Sq * Hq * (size_t)(D + 1) * sizeof(float);
+  return pl;
+}
+
+// ---------------------------------------------------------------------------
+// decode planning
+// ---------------------------------------------------------------------------
+struct DecodePlan {
+  int n_splits = 1;
+  int chunk = DEC_TILE;
+  int n_hblk = 1;
+  size_t ws_bytes = 0;
+};
+
+DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_layout layout,
+                       int num_splits, bool allow_split) {
+  DecodePlan pl;
+  const int tiles = std::max(1, ceil_div(max_seq_len, DEC_TILE));
+  int64_t units;
+  int64_t target;
+  if (layout == FA_KV_MLA_SHARED) {
+    pl.n_hblk = ceil_div(Hq, MLA_HEADS_PER_WG);
+    units = (int64_t)B * pl.n_hblk;   // one workgroup per unit
+    target = planner_cus();           // one 4-wave workgroup per CU
+  } else {
+    pl.n_hblk = ceil_div(Hq / Hkv, 16);
+    units = (int64_t)B * Hkv * pl.n_hblk;  // one wave per unit
+    target = 8 * (int64_t)planner_cus();   // two waves per SIMD
+  }
+  int S = 1;
+  if (allow_split && units > 0) {
+    int req = num_splits > 0 ? num_splits : env_int("FA_DECODE_SPLITS", 0);
+    if (req > 0) {
+      S = req;
+    } else {
+      // Split while the grid is short of the target, keeping >= 8 tiles
+      // (256 tokens) per split.
+      const int64_t want = (target + units - 1) / units;
+      S = (int)std::min<int64_t>(want, std::max(1, tiles / 8));
+    }
+    S = std::max(1, std::min(S, tiles));
+  }
+  pl.chunk = ceil_div(tiles, S) * DEC_TILE;
+  pl.n_splits = ceil_div(std::max(1, max_seq_len), pl.chunk);
+  if (pl.n_splits < 1) pl.n_splits = 1;
+  if (pl.n_splits > 1)
+    pl.ws_bytes = (size_t)pl.n_splits * B * Hq * (size_t)(D_v + 1) * sizeof(float);
+  return pl;
+}
+
+int check_prefill(const void* q, const void* k, const void* v, void* o, const float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, fa_dtype in_dtype,
+                  fa_dtype out_dtype) {
+  if (B < 1 || Hq < 1 || Hkv < 1 || Sq < 0 || Skv < 0 || Hq % Hkv != 0) return FA_ERR_SHAPE;
+  if (D != 64 && D != 128) return FA_ERR_UNSUPPORTED;
+  if (in_dtype != FA_BF16 && in_dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (out_dtype != FA_BF16 && out_dtype != FA_FP16 && out_dtype != FA_FP32)
+    return FA_ERR_UNSUPPORTED;
+  if (Sq > 0 && (!q || !o)) return FA_ERR_NULL;
+  if (Skv > 0 && (!k || !v)) return FA_ERR_NULL;
+  if ((q && !aligned16(q)) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
+      (o && !aligned16(o)) || (lse && !aligned4(lse)))
+    return FA_ERR_ALIGN;
+  if ((int64_t)B * Hq * ceil_div(Sq, PF_BM) > kMaxGrid) return FA_ERR_SHAPE;
+  return FA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fa_version(void) { return "0.1.0"; }
+
+const char* fa_strerror(int status) {
+  switch (status) {
+    case FA_OK: return "ok";
+    case FA_ERR_NULL: return "a required pointer is NULL";
+    case FA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case FA_ERR_UNSUPPORTED: return "unsupported head size or dtype";
+    case FA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
+    case FA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
+    case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
+    default: return "unknown status";
+  }
+}
+
+size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal) {
+  (void)Hkv;
+  (void)causal;
+  if (B < 1 || Hq < 1 || Sq < 1 || Skv < 0 || (D != 64 && D != 128)) return 0;
+  return plan_prefill(B, Hq, Sq, Skv, D, true).ws_bytes;
+}
+
+int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                  fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_prefill(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, in_dtype, out_dtype);
+  if (rc != FA_OK) return rc;
+  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
+  if (Sq == 0) return FA_OK;
+  const PrefillPlan pl = plan_prefill(B, Hq, Sq, Skv, D, workspace != nullptr);
+  if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
+  if ((int64_t)B * Hq * pl.n_qtiles * pl.n_splits > kMaxGrid) return FA_ERR_SHAPE;
+  if (pl.n_splits > 1 && (int64_t)B * Sq * Hq > INT_MAX) return FA_ERR_SHAPE;
+
+  PrefillParams p{};
+  p.q = q;
+  p.k = k;
+  p.v = v;
+  p.o = o;
+  p.lse = lse;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.Sq = Sq;
+  p.Skv = Skv;
+  p.n_qtiles = pl.n_qtiles;
+  p.n_splits = pl.n_splits;
+  p.scale = scale;
+  p.scale_log2 = scale * 1.4426950408889634f;
+  const int64_t rows = (int64_t)B * Sq * Hq;
+  if (pl.n_splits > 1) {
+    p.part_o = (float*)workspace;
+    p.part_lse = p.part_o + (size_t)pl.n_splits * rows * D;
+  }
+  const InType it = in_dtype == FA_BF16 ? InType::bf16 : InType::f16;
+  const OutType ot = out_dtype == FA_BF16 ? OutType::bf16
+                     : out_dtype == FA_FP16 ? OutType::f16
+                                            : OutType::f32;
+  if (launch_prefill(p, D, it, ot, causal != 0, stream) != hipSuccess) return FA_ERR_HIP;
+  if (pl.n_splits > 1) {
+    CombineParams c{};
+    c.part_o = p.part_o;
+    c.part_lse = p.part_lse;
+    c.o = o;
+    c.lse = lse;
+    c.rows = (int)rows;
+    c.D = D;
+    c.n_splits = pl.n_splits;
+    c.Sq = Sq;
+    c.Hq = Hq;
+    if (launch_combine(c, ot, stream) != hipSuccess) return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+int fa_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+               int Sq, int Skv, int D, int causal, float scale, hipStream_t stream) {
+  return fa_prefill_ex(q, k, v, o, nullptr, B, Hq, Hkv, Sq, Skv, D, causal, scale, FA_BF16,
+                       FA_BF16, nullptr, 0, stream);
+}
+
+static int check_decode(const void* q, const void* kv_pool, int num_pages,
+                        const int32_t* page_table,
+                        const int32_t* seq_lens, void* o, const float* lse, int B, int Hq,
+                        int Hkv, int D_qk, int D_v, int page_size, int max_pages_per_seq,
+                        int max_seq_len, fa_kv_layout layout, fa_dtype dtype) {
+  if (B < 0 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || page_size < 1 || max_pages_per_seq < 1 ||
+      max_seq_len < 0 || num_pages < 1)
+    return FA_ERR_SHAPE;
+  if ((int64_t)max_pages_per_seq * page_size < max_seq_len) return FA_ERR_SHAPE;
+  if (layout == FA_KV_SPLIT) {
+    if (D_qk != 128 || D_v != 128) return FA_ERR_UNSUPPORTED;
+  } else if (layout == FA_KV_MLA_SHARED) {
+    if (D_qk != 576 || D_v != 512) return FA_ERR_UNSUPPORTED;
+    if (Hkv != 1) return FA_ERR_SHAPE;
+  } else {
+    return FA_ERR_UNSUPPORTED;
+  }
+  if (dtype != FA_BF16 && dtype != FA_FP16) return FA_ERR_UNSUPPORTED;
+  if (B > 0 && (!q || !kv_pool || !page_table || !seq_lens || !o)) return FA_ERR_NULL;
+  if ((q && !aligned16(q)) || (kv_pool && !aligned16(kv_pool)) || (o && !aligned16(o)) ||
+      (page_table && !aligned4(page_table)) || (seq_lens && !aligned4(seq_lens)) ||
+      (lse && !aligned4(lse)))
+    return FA_ERR_ALIGN;
+  return FA_OK;
+}
+
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                                int max_seq_len, fa_kv_layout layout, int num_splits) {
+  (void)D_qk;
+  (void)page_size;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seq_len < 0 || D_v < 1) return 0;
+  return plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, true).ws_bytes;
+}
+
+int fa_decode_num_splits(int B, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                         int max_seq_len, fa_kv_layout layout, int num_splits) {
+  (void)D_qk;
+  (void)page_size;
+  if (B < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seq_len < 0 || D_v < 1) return 1;
+  return plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, true).n_splits;
+}
+
+int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
+                    const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                    int B, int Hq, int Hkv,
+                    int D_qk, int D_v, int page_size, int max_pages_per_seq, int max_seq_len,
+                    fa_kv_layout layout, float scale, int num_splits, fa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  int rc = check_decode(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Hq, Hkv, D_qk, D_v,
+                        page_size, max_pages_per_seq, max_seq_len, layout, dtype);
+  if (rc != FA_OK) return rc;
+  if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
+  if (B == 0) return FA_OK;
+  const DecodePlan pl =
+      plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, workspace != nullptr);
+  if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
+  const int64_t rows = (int64_t)B * Hq;
+  if (rows > INT_MAX) return FA_ERR_SHAPE;
+  float* part_o = nullptr;
+  float* part_lse = nullptr;
+  if (pl.n_splits > 1) {
+    part_o = (float*)workspace;
+    part_lse = part_o + (size_t)pl.n_splits * rows * D_v;
+  }
+  const InType it = dtype == FA_BF16 ? InType::bf16 : InType::f16;
+  hipError_t e;
+  if (layout == FA_KV_MLA_SHARED) {
+    DecodeMlaParams p{};
+    p.q = q;
+    p.pool = kv_pool;
+    p.page_table = page_table;
+    p.seq_lens = seq_lens;
+    p.o = o;
+    p.lse = lse;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.page_size = page_size;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    p.max_seq_len = max_seq_len;
+    p.n_hblk = pl.n_hblk;
+    p.chunk = pl.chunk;
+    p.n_splits = pl.n_splits;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    if ((int64_t)B * p.n_hblk * p.n_splits > kMaxGrid) return FA_ERR_SHAPE;
+    e = launch_decode_mla(p, it, stream);
+  } else {
+    DecodeSplitParams p{};
+    p.q = q;
+    p.pool = kv_pool;
+    p.page_table = page_table;
+    p.seq_lens = seq_lens;
+    p.o = o;
+    p.lse = lse;
+    p.part_o = part_o;
+    p.part_lse = part_lse;
+    p.B = B;
+    p.Hq = Hq;
+    p.Hkv = Hkv;
+    p.page_size = page_size;
+    p.max_pages = max_pages_per_seq;
+    p.num_pages = num_pages;
+    p.max_seq_len = max_seq_len;
+    p.n_hblk = pl.n_hblk;
+    p.chunk = pl.chunk;
+    p.n_splits = pl.n_splits;
+    const int64_t units = (int64_t)B * Hkv * pl.n_hblk * pl.n_splits;
+    if (units > kMaxGrid) return FA_ERR_SHAPE;
+    p.n_units = (int)units;
+    p.scale = scale;
+    p.scale_log2 = scale * 1.4426950408889634f;
+    e = launch_decode_split(p, it, stream);
+  }
+  if (e != hipSuccess) return FA_ERR_HIP;
+  if (pl.n_splits > 1) {
+    CombineParams c{};
+    c.part_o = part_o;
+    c.part_lse = part_lse;
+    c.o = o;
+    c.lse = lse;
+    c.rows = (int)rows;
+    c.D = D_v;
+    c.n_splits = pl.n_splits;
+    c.Sq = 1;
+    c.Hq = Hq;
+    if (launch_combine(c, dtype == FA_BF16 ? OutType::bf16 : OutType::f16, stream) != hipSuccess)
+      return FA_ERR_HIP;
+  }
+  return FA_OK;
+}
+
+}  // extern "C"

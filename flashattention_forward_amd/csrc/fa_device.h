@@ -1,0 +1,127 @@
+// Device helpers shared by the gfx950 attention kernels: vector types, 16-byte
+// memory access, bf16/fp16 packing and the MFMA shapes the kernels use.
+//
+// MFMA accumulator layouts relied on (CDNA3/CDNA4 matrix cores, wave64):
+//   v_mfma_f32_32x32x16_{bf16,f16}: A row m = lane % 32, B column n = lane % 32,
+//     each lane supplying 8 consecutive-k elements of its row/column; the 16
+//     accumulators of lane l hold D[8*(i/4) + 4*(l/32) + i%4][l % 32], i = 0..15.
+//   v_mfma_f32_16x16x32_{bf16,f16}: A row m = lane % 16, B column n = lane % 16;
+//     the 4 accumulators of lane l hold D[4*(l/16) + i][l % 16], i = 0..3.
+// A and B use the same (lane group, slot) -> k assignment, so any consistent
+// relabelling of the contraction index between the two operands is exact.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+
+struct bf16_t {};  // tag types for the 16-bit input formats
+struct f16_t {};
+
+template <typename T> struct in_traits;
+template <> struct in_traits<bf16_t> {
+  typedef bf16x8 vec8;
+  // Pack two fp32 into two bf16 (round to nearest even) in one dword.
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    bf16x2 v = {(__bf16)a, (__bf16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  }
+};
+template <> struct in_traits<f16_t> {
+  typedef f16x8 vec8;
+  static __device__ __forceinline__ uint32_t pack2(float a, float b) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    f16x2 v = {(_Float16)a, (_Float16)b};
+    return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+  static __device__ __forceinline__ f32x4 mma16(u32x4 a, u32x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+};
+
+// Output element stores. `n` consecutive fp32 values go to `dst` (n = 4).
+struct out_bf16 {};
+struct out_f16 {};
+struct out_f32 {};
+
+__device__ __forceinline__ void store4(out_f32, void* dst, float a, float b, float c, float d) {
+  *(f32x4*)dst = f32x4{a, b, c, d};
+}
+__device__ __forceinline__ void store4(out_bf16, void* dst, float a, float b, float c, float d) {
+  *(u32x2*)dst = u32x2{in_traits<bf16_t>::pack2(a, b), in_traits<bf16_t>::pack2(c, d)};
+}
+__device__ __forceinline__ void store4(out_f16, void* dst, float a, float b, float c, float d) {
+  *(u32x2*)dst = u32x2{in_traits<f16_t>::pack2(a, b), in_traits<f16_t>::pack2(c, d)};
+}
+template <typename O> struct out_size;
+template <> struct out_size<out_f32> { static constexpr int bytes = 4; };
+template <> struct out_size<out_bf16> { static constexpr int bytes = 2; };
+template <> struct out_size<out_f16> { static constexpr int bytes = 2; };
+
+__device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
+
+// Select the 16-bit halves of two dwords: lo16(a) | lo16(b) << 16 and
+// hi16(a) | hi16(b) << 16 (v_perm_b32 byte selects).
+__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x05040100u);
+}
+__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ds_read_b64_tr_b16: within each group of 16 lanes, lane j passes the address
+// of row r0 + j / 4, columns c0 + 4 * (j % 4) .. + 3 of a row-major 16-bit
+// matrix in LDS and receives column c0 + j of rows r0 .. r0 + 3 (4 elements).
+// It turns a row-major tile into MFMA operands that need consecutive rows per
+// lane (the keys of the P V product).
+__device__ __forceinline__ u32x2 lds_read_tr16(const char* p) {
+  typedef short s16x4 __attribute__((ext_vector_type(4)));
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  const s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// Swap values between lane l and lane l ^ 32.
+__device__ __forceinline__ float xor32(float v) { return __shfl_xor(v, 32, 64); }
+__device__ __forceinline__ float xor16(float v) { return __shfl_xor(v, 16, 64); }
+
+// Block index remap so that consecutive logical blocks share one XCD (the
+// hardware hands workgroups to the 8 XCDs round-robin by dispatch order).
+// Bijective on [0, n).
+__device__ __forceinline__ int xcd_remap(int pid, int n) {
+  const int x = pid & 7, s = pid >> 3;
+  const int q = n >> 3, r = n & 7;
+  return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
+}
+
+// Wave-local ordering of LDS accesses (all lanes' earlier LDS ops completed
+// before later ones are issued; also a compiler barrier).
+__device__ __forceinline__ void wave_lds_sync() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+}
+
+}  // namespace fa

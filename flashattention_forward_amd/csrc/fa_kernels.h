@@ -1,0 +1,86 @@
+// Kernel parameter blocks and host-side launch wrappers of the gfx950 kernels.
+// Shared by the kernel sources and the C-ABI front end (api.cpp).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fa {
+
+enum class InType { bf16 = 0, f16 = 1 };
+enum class OutType { bf16 = 0, f16 = 1, f32 = 2 };
+
+// Prefill: q, o [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D].
+struct PrefillParams {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;       // [B, Hq, Sq] or null
+  float* part_o;    // [S, B, Sq, Hq, D] fp32 when n_splits > 1
+  float* part_lse;  // [S, B, Sq, Hq]
+  int B, Hq, Hkv, Sq, Skv;
+  int n_qtiles;  // ceil(Sq / 128)
+  int n_splits;  // key splits per query tile
+  float scale;       // multiplies q.k
+  float scale_log2;  // scale * log2(e)
+};
+
+// Paged decode, separate K/V pool [P, 2, Hkv, page, D] (D = 128).
+struct DecodeSplitParams {
+  const void* q;  // [B, Hq, D]
+  const void* pool;
+  const int32_t* page_table;  // [B, max_pages]
+  const int32_t* seq_lens;    // [B]
+  void* o;                    // [B, Hq, D]
+  float* lse;                 // [B, Hq] or null
+  float* part_o;              // [S, B, Hq, D]
+  float* part_lse;            // [S, B, Hq]
+  int B, Hq, Hkv, page_size, max_pages, num_pages, max_seq_len;
+  int n_hblk;    // ceil((Hq / Hkv) / 16) head blocks per K/V head
+  int chunk;     // tokens per split (multiple of 32)
+  int n_splits;
+  int n_units;   // B * Hkv * n_hblk * n_splits
+  float scale, scale_log2;
+};
+
+// Paged MLA decode, shared pool [P, page, 576]; K = row, V = row[0:512].
+struct DecodeMlaParams {
+  const void* q;  // [B, Hq, 576]
+  const void* pool;
+  const int32_t* page_table;
+  const int32_t* seq_lens;
+  void* o;  // [B, Hq, 512]
+  float* lse;
+  float* part_o;  // [S, B, Hq, 512]
+  float* part_lse;
+  int B, Hq, page_size, max_pages, num_pages, max_seq_len;
+  int n_hblk;  // ceil(Hq / 64)
+  int chunk;   // tokens per split (multiple of 32)
+  int n_splits;
+  float scale, scale_log2;
+};
+
+// Split-KV log-sum-exp combine. Rows are in output order r = (b * Sq + i) * Hq + h;
+// part_o [S, rows, D], part_lse [S, rows]; o [rows, D]; lse index (b * Hq + h) * Sq + i.
+struct CombineParams {
+  const float* part_o;
+  const float* part_lse;
+  void* o;
+  float* lse;
+  int rows, D, n_splits, Sq, Hq;
+};
+
+hipError_t launch_prefill(const PrefillParams& p, int D, InType it, OutType ot, bool causal,
+                          hipStream_t stream);
+hipError_t launch_decode_split(const DecodeSplitParams& p, InType it, hipStream_t stream);
+hipError_t launch_decode_mla(const DecodeMlaParams& p, InType it, hipStream_t stream);
+hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream);
+
+// Tile constants the host planner needs.
+constexpr int PF_BM = 128;  // query rows per prefill workgroup (4 waves x 32)
+constexpr int PF_BN = 64;   // keys per prefill tile
+constexpr int DEC_TILE = 32;  // tokens per decode tile
+constexpr int MLA_HEADS_PER_WG = 64;
+
+}  // namespace fa

@@ -1,0 +1,159 @@
+/*
+ * fa.h -- C ABI of the MI355X (gfx950) attention forward library (libfa.so).
+ *
+ * The operation is the fused attention forward pass
+ *
+ *     O = softmax(scale * Q K^T + mask) V
+ *
+ * computed tile by tile with an online (running max / running sum) softmax, in
+ * the two workloads the pages turn on:
+ *
+ *  - prefill over microbatches with grouped-query heads ("CUDA: fix FA
+ *    occupancy, optimize tile kernel", llama.cpp: opening paragraph -- tile FA
+ *    kernel, KQ accumulators compressed to 16-bit before the second product, the
+ *    GQA optimisation -- and the "Performance changes" microbatch sweep);
+ *  - paged-KV decode, including MLA where K and V are one compressed-KV matrix
+ *    ("perf: FlashAttention-3 style MLA PageAttention", FlashInfer: change list
+ *    item 4, and "Results" for batch x seq_len x 64 heads at page_size = 1).
+ *
+ * Conventions shared by every entry point:
+ *  - All tensor pointers are DEVICE pointers owned by the caller. The library
+ *    allocates no device memory and keeps no pointer after a call returns.
+ *  - Layouts are fixed, row-major, last index fastest; there are no strides.
+ *  - Every call validates its arguments on the host first. A negative status
+ *    means nothing was enqueued. Status 0 means the kernels were enqueued on
+ *    `stream` (0 = the default stream); the call does not synchronise, so a
+ *    fault inside a kernel surfaces at the caller's next synchronisation.
+ *  - The mask is none (causal = 0) or causal aligned bottom-right: query i of
+ *    Sq sits at absolute position Skv - Sq + i and sees keys j <= Skv - Sq + i.
+ *    With Sq = Skv this is ordinary lower-triangular causal attention. A query
+ *    with no visible key (Sq > Skv, or an empty sequence) gets O = 0 and
+ *    lse = -infinity.
+ *  - Grouped-query heads: query head h reads K/V head h / (Hq / Hkv).
+ *  - lse (optional, may be NULL) is the natural-log log-sum-exp of the scaled
+ *    scores of a row, in fp32.
+ *  - Tensor base pointers must be 16-byte aligned (lse, page tables and
+ *    sequence lengths: 4-byte aligned).
+ *  - Calls on one stream are ordered; calls that share a workspace must not
+ *    run concurrently on different streams.
+ */
+#ifndef FA_H
+#define FA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FA_BF16 = 0, FA_FP16 = 1, FA_FP32 = 2 } fa_dtype;
+
+/* Paged KV pool layouts.
+ *  FA_KV_SPLIT:      pool [num_pages, 2 (K, V), Hkv, page_size, D]; D_qk == D_v.
+ *  FA_KV_MLA_SHARED: pool [num_pages, page_size, D_qk]; one row per token that is
+ *                    both the key (all D_qk columns, [ckv | kpe]) and the value
+ *                    (its first D_v columns, ckv). Hkv must be 1.
+ * Token t of sequence b is in page page_table[b * max_pages_per_seq + t / page_size]
+ * at slot t % page_size. */
+typedef enum { FA_KV_SPLIT = 0, FA_KV_MLA_SHARED = 1 } fa_kv_layout;
+
+enum {
+  FA_OK = 0,
+  FA_ERR_NULL = -1,        /* a required pointer is NULL */
+  FA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  FA_ERR_UNSUPPORTED = -3, /* head size / dtype combination not built */
+  FA_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
+  FA_ERR_WORKSPACE = -5,   /* workspace smaller than the plan needs */
+  FA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+};
+
+/*
+ * Prefill attention, bf16 in and bf16 out.
+ *   q, o [B, Sq, Hq, D]; k, v [B, Skv, Hkv, D]   (bf16)
+ *   D in {64, 128}; Hq % Hkv == 0; B, Hq, Hkv, D >= 1; Sq, Skv >= 0.
+ *   scale multiplies Q K^T (usually 1/sqrt(D)).
+ * Never splits the keys and needs no workspace. Same as fa_prefill_ex with
+ * in_dtype = out_dtype = FA_BF16, lse = NULL and no workspace.
+ */
+int fa_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,
+               int Sq, int Skv, int D, int causal, float scale, hipStream_t stream);
+
+/*
+ * Prefill attention, full form.
+ *   in_dtype  FA_BF16 or FA_FP16 (q, k, v)
+ *   out_dtype FA_BF16, FA_FP16 or FA_FP32 (o)
+ *   lse       [B, Hq, Sq] fp32, or NULL
+ *   workspace device memory for split-KV partial results, or NULL. With NULL
+ *             the keys are never split. Otherwise the launch planner may split
+ *             the keys of long rows over several workgroups and merge the parts
+ *             with a log-sum-exp combine kernel; workspace_bytes must then be at
+ *             least fa_prefill_workspace_size(...) for the same shape, or the
+ *             call fails with FA_ERR_WORKSPACE. The workspace holds no state
+ *             between calls.
+ */
+int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                  fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace the planner may use for this prefill shape (0 if it never
+ * splits it). Pure host function: needs no GPU. Environment variable
+ * FA_PREFILL_SPLITS forces a split count (tuning); FA_NUM_CUS sets the compute
+ * units planned for (default 256). */
+size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal);
+
+/*
+ * Paged-KV decode: one query token per sequence, attending to every cached
+ * token of its sequence (no mask).
+ *   q           [B, Hq, D_qk]  (dtype)
+ *   kv_pool     see fa_kv_layout (dtype)
+ *   num_pages   pages in kv_pool (>= 1). A page id outside [0, num_pages) is
+ *               never dereferenced: its tokens read as zero keys and values
+ *               (a wrong table gives wrong numbers, not a memory fault).
+ *   page_table  [B, max_pages_per_seq] int32 page ids (entries past a sequence's
+ *               last page are never read)
+ *   seq_lens    [B] int32, each in [0, max_seq_len] (device memory); values are
+ *               clamped to that range on the device
+ *   o           [B, Hq, D_v] (dtype)
+ *   lse         [B, Hq] fp32, or NULL
+ *   (D_qk, D_v) (128, 128) with FA_KV_SPLIT, (576, 512) with FA_KV_MLA_SHARED
+ *   page_size   >= 1; max_pages_per_seq * page_size >= max_seq_len
+ *   max_seq_len host-side upper bound of seq_lens (sizes the grid)
+ *   num_splits  0 = let the planner choose; n >= 1 asks for n key splits per
+ *               sequence (clamped to what the shape allows)
+ *   dtype       FA_BF16 or FA_FP16
+ *   workspace   partial results of split-KV, or NULL (then num_splits is 1)
+ * Pool slots that no token of a sequence owns (tail slots, spare pages) are
+ * never read as data, so they may hold anything, NaN included.
+ */
+int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
+                    const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                    int B, int Hq, int Hkv,
+                    int D_qk, int D_v, int page_size, int max_pages_per_seq, int max_seq_len,
+                    fa_kv_layout layout, float scale, int num_splits, fa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fa_decode_paged may use for this shape and split request
+ * (0 if it would not split). Pure host function. */
+size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                                int max_seq_len, fa_kv_layout layout, int num_splits);
+
+/* The number of key splits fa_decode_paged would use with a workspace (>= 1).
+ * Pure host function. Planning assumes the 256 compute units of gfx950 parts
+ * (environment variable FA_NUM_CUS overrides it). */
+int fa_decode_num_splits(int B, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                         int max_seq_len, fa_kv_layout layout, int num_splits);
+
+/* Static text for a status code. */
+const char* fa_strerror(int status);
+
+/* Library version, e.g. "0.1.0". */
+const char* fa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FA_H */

@@ -1,0 +1,141 @@
+"""The C-ABI library loads, exports every symbol its header declares, and
+rejects bad arguments on the host before any launch (CPU only: no call here
+reaches a kernel)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fa.h")
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import flashattention_forward_amd as fa
+    return fa
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(fa_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_entry_points():
+    names = declared_functions()
+    for n in ["fa_prefill", "fa_prefill_ex", "fa_decode_paged", "fa_prefill_workspace_size",
+              "fa_decode_workspace_size", "fa_strerror"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(fa):
+    lib = ctypes.CDLL(fa.LIB_PATH)
+    for n in declared_functions():
+        assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
+
+
+def test_strerror_and_version(fa):
+    assert fa.fa_strerror(0) == "ok"
+    assert "workspace" in fa.fa_strerror(-5)
+    assert fa.fa_strerror(12345) == "unknown status"
+    assert re.match(r"\d+\.\d+\.\d+", fa.fa_version())
+
+
+def _err(fn, *a, **k):
+    import flashattention_forward_amd as fa
+    with pytest.raises(fa.FaError) as e:
+        fn(*a, **k)
+    return e.value.status
+
+
+A = 1 << 20  # a 16-byte aligned fake address: never dereferenced by these calls
+
+
+def test_prefill_validation(fa):
+    f = fa.fa_prefill_ex
+    args = dict(B=1, Hq=4, Hkv=2, Sq=16, Skv=16, D=64, causal=1, scale=0.1, in_dtype=fa.FA_BF16,
+                out_dtype=fa.FA_BF16)
+
+    def call(q=A, k=A, v=A, o=A, lse=None, ws=None, ws_bytes=0, **kw):
+        a = dict(args)
+        a.update(kw)
+        return f(q, k, v, o, lse, a["B"], a["Hq"], a["Hkv"], a["Sq"], a["Skv"], a["D"],
+                 a["causal"], a["scale"], a["in_dtype"], a["out_dtype"], ws, ws_bytes, stream=0)
+
+    assert _err(call, q=None) == -1
+    assert _err(call, v=None) == -1
+    assert _err(call, Hkv=3) == -2
+    assert _err(call, B=0) == -2
+    assert _err(call, Sq=-1) == -2
+    assert _err(call, D=96) == -3
+    assert _err(call, in_dtype=fa.FA_FP32) == -3
+    assert _err(call, out_dtype=7) == -3
+    assert _err(call, q=A + 8) == -4
+    assert _err(call, lse=A + 2) == -4
+    assert _err(call, ws=A + 4) == -4
+    # a plan that splits the keys needs the full workspace
+    big = dict(B=1, Hq=4, Hkv=4, Sq=128, Skv=8192, D=128)
+    need = fa.fa_prefill_workspace_size(1, 4, 4, 128, 8192, 128, 0)
+    assert need > 0
+    assert _err(call, ws=A, ws_bytes=need - 4, **big) == -5
+    # nothing to do: returns before any launch
+    call(Sq=0)
+    assert fa.fa_prefill(None, None, None, None, 1, 1, 1, 0, 0, 64, 0, 1.0, stream=0) is None
+
+
+def test_prefill_workspace_size_rules(fa):
+    assert fa.fa_prefill_workspace_size(1, 32, 8, 512, 512, 128, 1) == 0  # short keys: no split
+    ws = fa.fa_prefill_workspace_size(1, 32, 8, 512, 16384, 128, 1)
+    rows = 512 * 32
+    assert ws % (rows * 129 * 4) == 0 and ws // (rows * 129 * 4) in (2, 4, 8, 16)
+    assert fa.fa_prefill_workspace_size(0, 1, 1, 1, 1, 64, 0) == 0
+
+
+def test_decode_validation(fa):
+    f = fa.fa_decode_paged
+
+    def call(q=A, pool=A, npages=10, pt=A, sl=A, o=A, lse=None, B=2, Hq=8, Hkv=2, Dqk=128,
+             Dv=128, ps=16, maxp=4, maxlen=64, layout=fa.FA_KV_SPLIT, splits=0,
+             dtype=fa.FA_BF16, ws=None, wsb=0):
+        return f(q, pool, npages, pt, sl, o, lse, B, Hq, Hkv, Dqk, Dv, ps, maxp, maxlen, layout,
+                 0.1, splits, dtype, ws, wsb, stream=0)
+
+    assert _err(call, pool=None) == -1
+    assert _err(call, sl=None) == -1
+    assert _err(call, Hkv=3) == -2
+    assert _err(call, ps=0) == -2
+    assert _err(call, maxp=3, maxlen=64) == -2  # 3 pages of 16 < 64 tokens
+    assert _err(call, npages=0) == -2
+    assert _err(call, Dqk=64, Dv=64) == -3
+    assert _err(call, layout=fa.FA_KV_MLA_SHARED) == -3  # needs (576, 512)
+    assert _err(call, layout=fa.FA_KV_MLA_SHARED, Dqk=576, Dv=512, Hkv=2) == -2
+    assert _err(call, layout=5) == -3
+    assert _err(call, dtype=fa.FA_FP32) == -3
+    assert _err(call, o=A + 2) == -4
+    assert _err(call, pt=A + 1) == -4
+    need = fa.fa_decode_workspace_size(2, 8, 2, 128, 128, 16, 4096, fa.FA_KV_SPLIT, 4)
+    assert need == 4 * 2 * 8 * 129 * 4
+    assert _err(call, maxp=256, maxlen=4096, splits=4, ws=A, wsb=need - 16) == -5
+    call(B=0)  # empty batch: nothing enqueued
+
+
+def test_decode_split_planning(fa):
+    # MLA: 128 sequences of 2048 tokens, 64 heads -> 2 splits fill 256 CUs
+    assert fa.fa_decode_num_splits(128, 64, 1, 576, 512, 1, 2048, fa.FA_KV_MLA_SHARED) == 2
+    # GQA, 4 sequences x 8 K/V heads: many splits over 32768 tokens
+    s = fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT)
+    assert 16 <= s <= 128
+    # explicit request is honoured (clamped to the 32-token tiles available)
+    assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT, 3) == 3
+    assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 40, fa.FA_KV_SPLIT, 8) == 2
+    assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 0, fa.FA_KV_SPLIT) == 1
+    assert fa.fa_decode_workspace_size(4, 32, 8, 128, 128, 16, 100, fa.FA_KV_SPLIT, 1) == 0
+
+
+def test_binding_rejects_host_tensors(fa):
+    import torch
+    x = torch.zeros(16, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        fa.fa_prefill(x, x, x, x, 1, 1, 1, 1, 1, 64, 0, 1.0, stream=0)

@@ -1,0 +1,171 @@
+"""GPU parity of the prefill path against the CPU oracle, through the C ABI.
+
+Small shapes are compared element by element (several tiles, ragged tails,
+GQA, causal bottom-right with Sq < Skv and Sq > Skv); the full-size workloads
+(non-causal MHA 4x16x2048x64 and causal GQA 32 microbatches of 512 over 16384
+tokens) are compared on sampled rows the oracle computes one by one, in the
+launch configuration the bench times.
+"""
+import os
+
+import numpy as np
+import pytest
+
+import fa_inputs as fi
+import oracle
+from helpers import assert_lse, assert_parity, log, to_dev, to_f64
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def fa():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import flashattention_forward_amd as fa
+    return fa
+
+
+def _dtype_torch(name):
+    import torch
+    return {"bf16": torch.bfloat16, "fp16": torch.float16, "fp32": torch.float32}[name]
+
+
+def run(fa, inp, *, lse=True, allow_split=True, q=None, k=None, v=None):
+    import torch
+    q = to_dev(inp.q, inp.in_dtype) if q is None else q
+    k = to_dev(inp.k, inp.in_dtype) if k is None else k
+    v = to_dev(inp.v, inp.in_dtype) if v is None else v
+    res = fa.prefill(q, k, v, causal=inp.causal, scale=inp.scale,
+                     out_dtype=_dtype_torch(inp.out_dtype), return_lse=lse,
+                     allow_split=allow_split)
+    torch.cuda.synchronize()
+    return res
+
+
+SMALL = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, in, out
+    (2, 4, 2, 200, 333, 64, True, "bf16", "bf16"),
+    (2, 4, 2, 200, 333, 128, False, "bf16", "bf16"),
+    (1, 8, 2, 77, 77, 128, True, "fp16", "fp16"),
+    (1, 2, 1, 300, 100, 64, True, "bf16", "fp32"),   # Sq > Skv: leading rows see no key
+    (1, 2, 2, 1, 1000, 128, True, "bf16", "bf16"),   # one query
+    (3, 2, 1, 130, 1, 64, False, "bf16", "bf16"),    # one key
+    (1, 6, 3, 129, 700, 128, True, "bf16", "bf16"),
+    (1, 16, 1, 64, 64, 64, False, "fp16", "fp32"),   # G = 16
+    (2, 3, 3, 255, 255, 128, True, "fp16", "bf16"),
+]
+
+
+@pytest.mark.parametrize("shape", SMALL, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_small_parity(fa, shape):
+    B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
+    log(f"prefill small {shape}")
+    inp = fi.prefill_inputs(20, B, Hq, Hkv, Sq, Skv, D, causal, it, ot)
+    o, lse = run(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, it, f"prefill {shape}")
+    assert_lse(to_f64(lse), ref_lse, f"prefill {shape}")
+    if causal and Sq > Skv:
+        assert np.all(to_f64(o)[:, :Sq - Skv] == 0.0)
+
+
+def test_tiny_causal_fp16_fp32_out(fa):
+    """Workload 1 in full: B=1, 4 heads, 128 tokens, D=64, fp16 in, fp32 out."""
+    inp = fi.workload(1)
+    log("workload 1 tiny causal")
+    o, lse = run(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert o.dtype.itemsize == 4
+    assert_parity(to_f64(o), ref, "fp16", "workload 1")
+    assert_lse(to_f64(lse), ref_lse, "workload 1")
+
+
+@pytest.mark.parametrize("splits", ["none", "1", "2", "4", "8", "auto"])
+@pytest.mark.parametrize("causal", [True, False])
+def test_prefill_split_sweep(fa, splits, causal, monkeypatch):
+    """Every key-split count gives the oracle's result (the p4 practice of
+    checking every value of a tuning knob)."""
+    inp = fi.prefill_inputs(21, 1, 4, 2, 256, 2000, 128, causal, "bf16", "bf16")
+    if splits not in ("none", "auto"):
+        monkeypatch.setenv("FA_PREFILL_SPLITS", splits)
+    log(f"prefill split sweep splits={splits} causal={causal}")
+    o, lse = run(fa, inp, allow_split=splits != "none")
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, "bf16", f"splits={splits}")
+    assert_lse(to_f64(lse), ref_lse, f"splits={splits}")
+
+
+def test_prefill_no_keys(fa):
+    import torch
+    q = torch.randn(1, 40, 2, 64, device="cuda").to(torch.bfloat16)
+    k = torch.empty(1, 0, 2, 64, device="cuda", dtype=torch.bfloat16)
+    o, lse = fa.prefill(q, k, k.clone(), causal=False, scale=0.125, return_lse=True)
+    torch.cuda.synchronize()
+    assert torch.all(o == 0) and torch.all(torch.isneginf(lse))
+
+
+def test_causal_first_query_is_v0_exact(fa):
+    """Causal with Sq = Skv: row 0 sees only key 0, with weight exactly 1."""
+    inp = fi.prefill_inputs(22, 2, 4, 2, 150, 150, 128, True, "bf16", "bf16")
+    o, _ = run(fa, inp)
+    got = o[:, 0].view(dtype=__import__("torch").int16).cpu().numpy().view(np.uint16)
+    G = inp.Hq // inp.Hkv
+    want = np.repeat(inp.v[:, 0], G, axis=1)
+    np.testing.assert_array_equal(got, want)
+
+
+def test_mha_full_size_sampled(fa):
+    """Workload 2 in full (non-causal MHA B=4, 16 heads, 2048 tokens, D=64) on
+    2048 sampled rows."""
+    inp = fi.workload(2)
+    log("workload 2 full size")
+    o, lse = run(fa, inp)
+    o = to_f64(o)
+    lse = to_f64(lse)
+    r = np.random.default_rng(0)
+    rows = np.stack([r.integers(0, inp.B, 2048), r.integers(0, inp.Hq, 2048),
+                     r.integers(0, inp.Sq, 2048)], axis=1)
+    ref, ref_lse = oracle.prefill_rows(inp, rows)
+    got = o[rows[:, 0], rows[:, 2], rows[:, 1]]
+    assert_parity(got, ref, "bf16", "workload 2 sampled")
+    assert_lse(lse[rows[:, 0], rows[:, 1], rows[:, 2]], ref_lse, "workload 2 sampled")
+    assert np.isfinite(o).all()
+
+
+def test_gqa_ubatch_full_size_sampled(fa):
+    """Workload 3 in full: 32 microbatch calls (queries [512u, 512u+512) against
+    keys [0, 512(u+1)), causal bottom-right) with the bench's launch
+    configuration, checked on 16 sampled rows of every microbatch; the
+    concatenated output also matches one causal call over all 16384 tokens."""
+    import torch
+    inp = fi.workload(3)
+    UB = fi.UBATCH
+    log("workload 3 full size")
+    q = to_dev(inp.q, "bf16")
+    k = to_dev(inp.k, "bf16")
+    v = to_dev(inp.v, "bf16")
+    o = torch.empty_like(q)
+    lse = torch.empty((1, inp.Hq, inp.Sq), dtype=torch.float32, device="cuda")
+    n_ub = inp.Sq // UB
+    for u in range(n_ub):
+        Skv = UB * (u + 1)
+        ws_bytes = fa.fa_prefill_workspace_size(1, inp.Hq, inp.Hkv, UB, Skv, inp.D, 1)
+        ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+        fa.fa_prefill_ex(q[:, UB * u:UB * (u + 1)], k[:, :Skv], v[:, :Skv],
+                         o[:, UB * u:UB * (u + 1)], None, 1, inp.Hq, inp.Hkv, UB, Skv, inp.D, 1,
+                         inp.scale, fa.FA_BF16, fa.FA_BF16, ws, ws_bytes)
+    torch.cuda.synchronize()
+    r = np.random.default_rng(3)
+    rows = []
+    for u in range(n_ub):
+        for _ in range(16):
+            rows.append((0, int(r.integers(0, inp.Hq)), UB * u + int(r.integers(0, UB))))
+    rows = np.array(rows)
+    ref, _ = oracle.prefill_rows(inp, rows)
+    of = to_f64(o)
+    assert_parity(of[rows[:, 0], rows[:, 2], rows[:, 1]], ref, "bf16", "workload 3 sampled")
+    assert np.isfinite(of).all()
+    full, _ = fa.prefill(q, k, v, causal=True, scale=inp.scale, return_lse=True)
+    torch.cuda.synchronize()
+    assert_parity(of, to_f64(full), "bf16", "workload 3 ubatches vs one call")
