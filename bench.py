@@ -206,7 +206,7 @@ def main():
     dec_gbs = bytes4 * K / t_dec / 1e9
 
     sha_pf = source_sha("prefill.hip", "combine.hip", "fa_device.h")
-    sha_dec = source_sha("decode.hip", "combine.hip", "fa_device.h")
+    sha_dec = source_sha("decode_mla.hip", "combine.hip", "fa_device.h")
     tr_pf = traffic_for("prefill", sha_pf)
     tr_dec = traffic_for("decode_mla", sha_dec)
 

@@ -93,10 +93,12 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
   const int tiles = std::max(1, ceil_div(max_seq_len, DEC_TILE));
   int64_t units;
   int64_t target;
+  int min_splits = 1;
   if (layout == FA_KV_MLA_SHARED) {
     pl.n_hblk = ceil_div(Hq, MLA_HEADS_PER_WG);
     units = (int64_t)B * pl.n_hblk;   // one workgroup per unit
     target = planner_cus();           // one 4-wave workgroup per CU
+    min_splits = ceil_div(std::max(1, max_seq_len), MLA_MAX_CHUNK);
   } else {
     pl.n_hblk = ceil_div(Hq / Hkv, 16);
     units = (int64_t)B * Hkv * pl.n_hblk;  // one wave per unit
@@ -115,6 +117,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
     }
     S = std::max(1, std::min(S, tiles));
   }
+  S = std::max(S, min_splits);
   pl.chunk = ceil_div(tiles, S) * DEC_TILE;
   pl.n_splits = ceil_div(std::max(1, max_seq_len), pl.chunk);
   if (pl.n_splits < 1) pl.n_splits = 1;
@@ -192,8 +195,9 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   p.Skv = Skv;
   p.n_qtiles = pl.n_qtiles;
   p.n_splits = pl.n_splits;
-  p.scale = scale;
-  p.scale_log2 = scale * 1.4426950408889634f;
+  p.q_neg = scale < 0.f;
+  p.scale = std::fabs(scale);
+  p.scale_log2 = p.scale * 1.4426950408889634f;
   const int64_t rows = (int64_t)B * Sq * Hq;
   if (pl.n_splits > 1) {
     p.part_o = (float*)workspace;
@@ -311,8 +315,9 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     p.n_hblk = pl.n_hblk;
     p.chunk = pl.chunk;
     p.n_splits = pl.n_splits;
-    p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
+    p.q_neg = scale < 0.f;
+    p.scale = std::fabs(scale);
+    p.scale_log2 = p.scale * 1.4426950408889634f;
     if ((int64_t)B * p.n_hblk * p.n_splits > kMaxGrid) return FA_ERR_SHAPE;
     e = launch_decode_mla(p, it, stream);
   } else {
@@ -338,8 +343,9 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     const int64_t units = (int64_t)B * Hkv * pl.n_hblk * pl.n_splits;
     if (units > kMaxGrid) return FA_ERR_SHAPE;
     p.n_units = (int)units;
-    p.scale = scale;
-    p.scale_log2 = scale * 1.4426950408889634f;
+    p.q_neg = scale < 0.f;
+    p.scale = std::fabs(scale);
+    p.scale_log2 = p.scale * 1.4426950408889634f;
     e = launch_decode_split(p, it, stream);
   }
   if (e != hipSuccess) return FA_ERR_HIP;

@@ -124,4 +124,56 @@ __device__ __forceinline__ void wave_lds_sync() {
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 }
 
+// Workgroup barrier for LDS traffic only: this wave's LDS operations are
+// complete, then all waves meet. Unlike __syncthreads() it does not wait for
+// outstanding global loads, so prefetches stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most N of this wave's vector-memory operations are
+// outstanding (they retire in issue order).
+template <int N> __device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+
+// LDS byte address (offset in the workgroup's LDS) of a __shared__ pointer.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane l's 16 bytes from gsrc land at LDS address lds_base + 16 * l; lds_base
+// is wave-uniform and goes through M0, which is restored afterwards. (The
+// instruction's immediate offset is left at 0: it would move the LDS side too.)
+// Issued from inline assembly so the compiler does not add a full vmcnt(0)
+// wait before every later LDS read; callers wait with wait_vmcnt<N>(), which
+// counts these copies like any vector load (they retire in issue order).
+__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %2\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
+__device__ __forceinline__ u32x4 lds16(const char* p) { return *(const u32x4*)p; }
+
+// Flip the sign of the 8 bf16/fp16 values of a fragment (a negative scale is
+// applied as |scale| on -Q so the running max stays a max).
+__device__ __forceinline__ u32x4 neg16x8(u32x4 v) {
+  return v ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
+}
+
+// Online-softmax rescale threshold in log2 units: the running max is moved
+// only when a tile's max exceeds it by more than this, so probabilities stay
+// <= 2^8 and the O rescale (a pass over all accumulators) is rare.
+constexpr float RESCALE_LOG2 = 8.0f;
+
 }  // namespace fa

@@ -22,8 +22,9 @@ struct PrefillParams {
   int B, Hq, Hkv, Sq, Skv;
   int n_qtiles;  // ceil(Sq / 128)
   int n_splits;  // key splits per query tile
-  float scale;       // multiplies q.k
-  float scale_log2;  // scale * log2(e)
+  int q_neg;     // 1: the scale was negative; the kernel uses -Q and |scale|
+  float scale;       // |scale|, multiplies q.k
+  float scale_log2;  // |scale| * log2(e)
 };
 
 // Paged decode, separate K/V pool [P, 2, Hkv, page, D] (D = 128).
@@ -41,6 +42,7 @@ struct DecodeSplitParams {
   int chunk;     // tokens per split (multiple of 32)
   int n_splits;
   int n_units;   // B * Hkv * n_hblk * n_splits
+  int q_neg;
   float scale, scale_log2;
 };
 
@@ -56,8 +58,9 @@ struct DecodeMlaParams {
   float* part_lse;
   int B, Hq, page_size, max_pages, num_pages, max_seq_len;
   int n_hblk;  // ceil(Hq / 64)
-  int chunk;   // tokens per split (multiple of 32)
+  int chunk;   // tokens per split (multiple of 32, <= MLA_MAX_CHUNK)
   int n_splits;
+  int q_neg;
   float scale, scale_log2;
 };
 
@@ -82,5 +85,6 @@ constexpr int PF_BM = 128;  // query rows per prefill workgroup (4 waves x 32)
 constexpr int PF_BN = 64;   // keys per prefill tile
 constexpr int DEC_TILE = 32;  // tokens per decode tile
 constexpr int MLA_HEADS_PER_WG = 64;
+constexpr int MLA_MAX_CHUNK = 2048;  // tokens per MLA split (its row ids live in LDS)
 
 }  // namespace fa

@@ -14,16 +14,21 @@
 //    the row max is in-lane plus one exchange with lane l ^ 32;
 //  * the probabilities are rounded to 16 bits in registers and fed straight back
 //    as the B operand of O^T += V^T P^T. The contraction index of that product
-//    is relabelled to match the accumulator layout, and V is written to LDS
-//    transposed in that relabelled key order, so every MFMA operand read is one
-//    conflict-free 16-byte LDS load;
-//  * K/V tiles are double-buffered: global loads of tile t+1 are issued before
-//    the math of tile t and written to the other LDS buffer after it, one
-//    workgroup barrier per tile;
+//    is relabelled to match the accumulator layout; the V^T operand comes from
+//    the row-major V tile through the LDS transpose read (ds_read_b64_tr_b16);
+//  * K and V tiles go from global memory straight into LDS (global_load_lds,
+//    no register staging) into a ring of stages: the copy of tile t+1 is in
+//    flight while tile t is computed, and barriers wait on LDS traffic only;
+//  * tiles are stored chunk-major (16-byte chunk c of key row r at slot
+//    64 * c + r, V rows XOR-ed with 4 * (c & 3)), so a copy instruction is one
+//    chunk column of all 64 keys, and the K reads (16 rows of one chunk) and the
+//    transposed V reads (4 rows x 4 chunks) each touch distinct banks;
 //  * causal (bottom-right aligned) blocks stop at their last visible tile, waves
 //    skip tiles that none of their rows can see, and only tiles crossing the
 //    diagonal or the end of the keys are masked;
-//  * the exponent uses exp2 with scale * log2(e) folded into one FMA;
+//  * the exponent uses exp2 with scale * log2(e) folded into one FMA, and the
+//    running max moves only when it grows by more than 2^8, so the O
+//    accumulators are rarely rescaled;
 //  * a workgroup may process one of several key splits; it then writes its
 //    normalised partial O and log-sum-exp for a separate combine kernel.
 #include "fa_device.h"
@@ -31,82 +36,20 @@
 
 namespace fa {
 
-constexpr int PF_KPAD = 8;  // bf16 elements of padding per K row in LDS
-constexpr int PF_VPAD = 8;  // per transposed-V row
-
-template <int D> struct PfLds {
-  static constexpr int KS = D + PF_KPAD;      // K row stride (elements)
-  static constexpr int VS = PF_BN + PF_VPAD;  // V^T row stride (elements)
-  static constexpr int K_BYTES = PF_BN * KS * 2;
-  static constexpr int V_BYTES = D * VS * 2;
-  static constexpr int STAGE = K_BYTES + V_BYTES;
-  static constexpr int NK = PF_BN * D / 8 / 256;  // 16-byte K chunks per thread
-  static constexpr int NV_UNITS = 16 * (D / 8);   // (4 keys x 8 dims) V units per tile
+template <int D> struct PfCfg {
+  static constexpr int NCH = D / 8;                 // 16-byte chunks per key row
+  static constexpr int TILE = PF_BN * D * 2;        // bytes of one K (or V) tile
+  static constexpr int STAGE = 2 * TILE;            // K tile then V tile
+  static constexpr int NST = D == 64 ? 4 : 2;       // stages in the LDS ring
+  static constexpr int CPW = NCH / 4;               // chunk columns per wave (K and V each)
+  static constexpr int IPW = 2 * CPW;               // copy instructions per wave and tile
 };
-
-// Position of key `kg * 4` (kg = 4-key group 0..15 in a 64-key tile) in the
-// relabelled order of the P V contraction: within each 16 keys, swap bits 2, 3.
-__device__ __forceinline__ int vt_pos(int kg) {
-  return 16 * (kg >> 2) + 8 * (kg & 1) + 4 * ((kg >> 1) & 1);
-}
-
-template <int D, typename TI>
-struct TileRegs {
-  u32x4 k[PfLds<D>::NK];
-  u32x4 v[4];
-};
-
-template <int D, typename TI>
-__device__ __forceinline__ void load_tile(TileRegs<D, TI>& r, const char* kbase,
-                                          const char* vbase, int k0, int Skv, int row_bytes,
-                                          int tid) {
-  constexpr int CPR = D / 8;  // 16-byte chunks per row
-#pragma unroll
-  for (int i = 0; i < PfLds<D>::NK; ++i) {
-    const int id = tid + 256 * i;
-    const int row = id / CPR, col = id % CPR;
-    const int key = k0 + row;
-    r.k[i] = key < Skv ? ldg16(kbase + (int64_t)key * row_bytes + col * 16) : u32x4{0, 0, 0, 0};
-  }
-  if (tid < PfLds<D>::NV_UNITS) {
-    const int kg = tid / CPR, dc = tid % CPR;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int key = k0 + 4 * kg + j;
-      r.v[j] = key < Skv ? ldg16(vbase + (int64_t)key * row_bytes + dc * 16) : u32x4{0, 0, 0, 0};
-    }
-  }
-}
-
-template <int D, typename TI>
-__device__ __forceinline__ void store_tile(const TileRegs<D, TI>& r, char* stage, int tid) {
-  using L = PfLds<D>;
-  constexpr int CPR = D / 8;
-#pragma unroll
-  for (int i = 0; i < L::NK; ++i) {
-    const int id = tid + 256 * i;
-    const int row = id / CPR, col = id % CPR;
-    *(u32x4*)(stage + (row * L::KS + col * 8) * 2) = r.k[i];
-  }
-  if (tid < L::NV_UNITS) {
-    const int kg = tid / CPR, dc = tid % CPR;
-    char* vt = stage + L::K_BYTES + vt_pos(kg) * 2;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int d0 = dc * 8 + 2 * e;
-      *(u32x2*)(vt + d0 * L::VS * 2) =
-          u32x2{pack_lo(r.v[0][e], r.v[1][e]), pack_lo(r.v[2][e], r.v[3][e])};
-      *(u32x2*)(vt + (d0 + 1) * L::VS * 2) =
-          u32x2{pack_hi(r.v[0][e], r.v[1][e]), pack_hi(r.v[2][e], r.v[3][e])};
-    }
-  }
-}
 
 template <int D, typename TI, typename TO, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
-  using L = PfLds<D>;
+  using C = PfCfg<D>;
   using T = in_traits<TI>;
-  __shared__ __attribute__((aligned(16))) char smem[2 * L::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[C::NST * C::STAGE];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, h = lane >> 5;
@@ -148,9 +91,34 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   {
     const char* qrow = (const char*)p.q + (((int64_t)b * p.Sq + qi) * p.Hq + hq) * D * 2;
 #pragma unroll
-    for (int s = 0; s < D / 16; ++s)
-      qf[s] = q_ok ? ldg16(qrow + (16 * s + 8 * h) * 2) : u32x4{0, 0, 0, 0};
+    for (int s = 0; s < D / 16; ++s) {
+      const u32x4 v = q_ok ? ldg16(qrow + (16 * s + 8 * h) * 2) : u32x4{0, 0, 0, 0};
+      qf[s] = p.q_neg ? neg16x8(v) : v;
+    }
   }
+
+  // Copies of tile t into stage (t - t_begin) % NST. Wave w fills chunk columns
+  // n = CPW * w .. + CPW - 1 of K and of V; lane l copies key row l of K and key
+  // row l ^ 4 * (n & 3) of V (the V swizzle). Keys past the end are clamped to
+  // the last key: their scores are masked and their probabilities are 0.
+  const uint32_t smem_lds = lds_addr(smem);
+  auto issue = [&](int t) {
+    const uint32_t st = smem_lds + ((t - t_begin) % C::NST) * C::STAGE;
+    const int k0 = t * PF_BN;
+    const int kr = min(k0 + lane, p.Skv - 1);
+    const char* ksrc = kbase + (int64_t)kr * row_bytes + C::CPW * w * 16;
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int n = C::CPW * w + i;
+      dma16(ksrc + 16 * i, st + n * 1024);
+    }
+#pragma unroll
+    for (int i = 0; i < C::CPW; ++i) {
+      const int n = C::CPW * w + i;
+      const int vr = min(k0 + (lane ^ (4 * (n & 3))), p.Skv - 1);
+      dma16(vbase + (int64_t)vr * row_bytes + n * 16, st + C::TILE + n * 1024);
+    }
+  };
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -159,35 +127,47 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const float sl2 = p.scale_log2;
   const int q_last_wave = min(qw0 + 31, p.Sq - 1);
 
-  TileRegs<D, TI> regs;
-  if (t_begin < t_end) {
-    load_tile<D, TI>(regs, kbase, vbase, t_begin * PF_BN, p.Skv, row_bytes, tid);
-    store_tile<D, TI>(regs, smem, tid);
-  }
-  __syncthreads();
+  // Per-lane LDS offsets. K (A operand): row 32 * kb + c, chunk 2s + h.
+  const int koff = 1024 * h + 16 * c;
+  // V^T (A operand) by transpose reads: lane j = lane & 15 of 16-lane group gb
+  // = (lane >> 4) & 1 reads rows 16 jj + 4h + j/4 (then + 8) of chunk
+  // 4 db + 2 gb + e, e = (j & 3) >> 1, byte 8 * (j & 1); rows are XOR-ed with
+  // 4 * (chunk & 3) = 8 gb + 4 e.
+  const int j = lane & 15, gb = (lane >> 4) & 1, e = (j & 3) >> 1;
+  const int voffA = 1024 * (2 * gb + e) + 128 * gb + 64 * (h ^ e) + 16 * (j >> 2) + 8 * (j & 1);
+  const int voffB = voffA + 128 - 256 * gb;
+
+  for (int t = t_begin; t < min(t_end, t_begin + C::NST - 1); ++t) issue(t);
 
   for (int t = t_begin; t < t_end; ++t) {
-    const int st = (t - t_begin) & 1;
-    const bool more = t + 1 < t_end;
-    if (more) load_tile<D, TI>(regs, kbase, vbase, (t + 1) * PF_BN, p.Skv, row_bytes, tid);
+    // Wait for this wave's copies of tile t (later tiles may stay in flight).
+    if (C::NST >= 4 && t + 2 < t_end)
+      wait_vmcnt<2 * C::IPW>();
+    else if (C::NST >= 3 && t + 1 < t_end)
+      wait_vmcnt<C::IPW>();
+    else
+      wait_vmcnt<0>();
+    lds_barrier();
+    if (t + C::NST - 1 < t_end) issue(t + C::NST - 1);
 
     const int k0 = t * PF_BN;
     const bool active = !CAUSAL || k0 <= q_last_wave + off;
     if (active) {
-      const char* Ks = smem + st * L::STAGE;
-      const char* Vt = Ks + L::K_BYTES;
+      const char* Ks = smem + ((t - t_begin) % C::NST) * C::STAGE;
+      const char* Vs = Ks + C::TILE;
       f32x16 sacc[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = *(const u32x4*)(Ks + ((32 * kb + c) * L::KS + 16 * s + 8 * h) * 2);
+          const u32x4 a = lds16(Ks + koff + 2048 * s + 512 * kb);
           sacc[kb] = T::mma32(a, qf[s], sacc[kb]);
         }
       }
       const bool need_mask = (k0 + PF_BN > p.Skv) || (CAUSAL && k0 + PF_BN - 1 > qw0 + off);
+      // Masked keys: -inf for the max, probability forced to 0 below.
+      const int lim = !need_mask ? k0 + PF_BN : (CAUSAL ? min(p.Skv - 1, qi + off) : p.Skv - 1);
       if (need_mask) {
-        const int lim = CAUSAL ? min(p.Skv - 1, qi + off) : p.Skv - 1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -202,39 +182,46 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
       mx = fmaxf(mx, xor32(mx));
-      const float m_new = fmaxf(m_run, mx);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2((m_run - m_use) * sl2);
-      const float nb = -m_use * sl2;
-      float rs = 0.f;
+      // Lazy rescale: move the running max only when it grows by > 2^8.
+      const bool grow =
+          mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
+      if (__ballot(grow)) {
+        const float m_new = grow ? mx : m_run;
+        const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * sl2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+        m_run = m_new;
+      }
+      const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
       u32x4 pb[4];
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
         const int kb = jj >> 1, base = 8 * (jj & 1);
         float pv[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          pv[e] = fast_exp2(fmaf(sacc[kb][base + e], sl2, nb));
-          rs += pv[e];
+        for (int ee = 0; ee < 8; ++ee) {
+          pv[ee] = fast_exp2(fmaf(sacc[kb][base + ee], sl2, nb));
+          if (need_mask) {
+            const int i = base + ee;
+            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+            if (key > lim) pv[ee] = 0.f;
+          }
+          l_run += pv[ee];
         }
         pb[jj] = u32x4{T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
                        T::pack2(pv[6], pv[7])};
       }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const u32x4 a = *(const u32x4*)(Vt + ((32 * db + c) * L::VS + 16 * jj + 8 * h) * 2);
-          oacc[db] = T::mma32(a, pb[jj], oacc[db]);
+          const u32x2 ra = lds_read_tr16(Vs + voffA + 4096 * db + 256 * jj);
+          const u32x2 rb = lds_read_tr16(Vs + voffB + 4096 * db + 256 * jj);
+          oacc[db] = T::mma32(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb[jj], oacc[db]);
         }
       }
     }
-    if (more) store_tile<D, TI>(regs, smem + (st ^ 1) * L::STAGE, tid);
-    __syncthreads();
   }
 
   // Epilogue: both lane halves hold parts of the row sum.
