@@ -17,11 +17,10 @@
 //    resolved once per split into LDS, so no global load in the loop depends on
 //    another. Barriers wait on LDS only; each wave waits (vmcnt) for its own
 //    copies of the tile it is about to use;
-//  * a tile is stored chunk-major: the 16-byte chunk c of token row r sits at
-//    slot 32 * c + (r ^ 8 * (c & 1)). One copy instruction then fills two chunk
-//    columns, every lane copies the same token row in all of its 9 copies per
-//    tile (the address is a row base plus a constant), and both the key reads
-//    (16 consecutive rows of one chunk) and the transposed value reads
+//  * a tile is stored in 8 x 8 blocks of 16-byte chunks (blk_slot): one copy
+//    instruction moves 8 token rows x 128 contiguous bytes, wave w copies token
+//    rows 8w .. 8w + 7 (each lane the same row in all 9 of its copies), and both
+//    the key reads (16 rows of one chunk) and the transposed value reads
 //    (ds_read_b64_tr_b16: 8 rows x 2 chunks) touch 64 distinct banks;
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32 as in the other
 //    decode kernel; the running max moves only when it grows by more than 2^8,
@@ -41,8 +40,10 @@ constexpr int MLA_NST = 4;                         // LDS ring stages
 constexpr int MLA_STAGE = DEC_TILE * MLA_ROWB;     // 36864 bytes
 constexpr int MLA_IPW = DEC_TILE * MLA_NCH / 64 / 4;  // 9 copy instructions per wave and tile
 
-// LDS byte offset of chunk c of tile row r (chunk-major, rows XOR 8 on odd chunks).
-__device__ __forceinline__ int mla_slot(int c, int r) { return (32 * c + (r ^ (8 * (c & 1)))) * 16; }
+// LDS byte offset of chunk c of tile row r: block (r >> 3, c >> 3) of 9 per row band.
+__device__ __forceinline__ int mla_slot(int c, int r) {
+  return 16 * (64 * (9 * (r >> 3) + (c >> 3)) + blk_slot(r, c));
+}
 
 template <typename TI, int PS>
 __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
@@ -60,7 +61,6 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
   const int b = blk / p.n_hblk;
   const int head = hb * MLA_HEADS_PER_WG + 16 * w + c16;
   const bool hvalid = head < p.Hq;
-  const bool wave_active = hb * MLA_HEADS_PER_WG + 16 * w < p.Hq;
 
   const int seq_len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int t0 = split * p.chunk;
@@ -99,13 +99,13 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
 
   const char* pool = (const char*)p.pool;
   const uint32_t smem_lds = lds_addr(smem);
-  // Copy tile t into stage t % MLA_NST. Instruction i of wave w fills chunk
-  // columns 2n and 2n + 1 (n = 9w + i); lane l copies token row
-  // (l & 31) ^ 8 * (l >> 5) of the tile, chunk 2n + (l >> 5). Every wave issues
-  // exactly MLA_IPW copies per tile (the vmcnt waits count on it); rows without
-  // a valid token read pool row 0 and are zeroed before use.
-  const int dma_row = (lane & 31) ^ (8 * (lane >> 5));
-  const int dma_col = (18 * w + (lane >> 5)) * 16;
+  // Copy tile t into stage t % MLA_NST. Instruction i of wave w fills block
+  // (w, i): lane l copies chunk 8i + ((l >> 3) ^ (w & 1)) of token row
+  // 8w + ((l & 7) ^ 4 * ((l >> 4) & 1)) (the inverse of blk_slot). Every wave
+  // issues exactly MLA_IPW copies per tile (the vmcnt waits count on it); rows
+  // without a valid token read pool row 0 and are zeroed before use.
+  const int dma_row = 8 * w + ((lane & 7) ^ (4 * ((lane >> 4) & 1)));
+  const int dma_col = 16 * ((lane >> 3) ^ (w & 1));
   auto issue = [&](int t) {
     const uint32_t dst = smem_lds + (t % MLA_NST) * MLA_STAGE + MLA_IPW * w * 1024;
     const int tok = t * DEC_TILE + dma_row;
@@ -113,7 +113,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
     rid = rid < 0 ? 0 : rid;
     const char* src = pool + (int64_t)rid * MLA_ROWB + dma_col;
 #pragma unroll
-    for (int i = 0; i < MLA_IPW; ++i) dma16(src + 32 * i, dst + 1024 * i);
+    for (int i = 0; i < MLA_IPW; ++i) dma16(src + 128 * i, dst + 1024 * i);
   };
 
   f32x4 oacc[MLA_DV / 16];
@@ -122,12 +122,15 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = p.scale_log2;
 
-  // Key reads: rows 16 * kb + c16 of chunk 4s + gq.
-  const int koff = gq * 512 + ((c16 ^ (8 * (gq & 1))) * 16);
+  // Key reads: rows 16 * kb + c16 of chunk 4s + gq (mla_slot written out).
+  const int kp8 = c16 >> 3;
+  const int koff = 9216 * kp8 + 128 * (gq ^ kp8) + 16 * ((c16 & 7) ^ (4 * (gq >> 1)));
   // Transposed value reads, lane j = c16: rows 4gq + j/4 (and +16) of chunk
-  // 2db + e with e = (j & 3) >> 1, byte 8 * (j & 1) inside the chunk.
+  // 2db + e with e = (j & 3) >> 1, byte 8 * (j & 1) inside the chunk; the offset
+  // alternates with the parity of db.
   const int e = (c16 & 3) >> 1;
-  const int toff = 512 * e + (((4 * gq + (c16 >> 2)) ^ (8 * e)) * 16) + 8 * (c16 & 1);
+  const int tbase = 9216 * (gq >> 1) + 128 * (e ^ ((gq >> 1) & 1)) + 16 * (c16 >> 2) + 8 * (c16 & 1);
+  const int toffE = tbase + 64 * (gq & 1), toffO = tbase + 64 * ((gq & 1) ^ 1);
 
   for (int t = 0; t < min(n_tiles, MLA_NST - 1); ++t) issue(t);
 
@@ -156,14 +159,17 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
     }
     if (t + MLA_NST - 1 < n_tiles) issue(t + MLA_NST - 1);
 
-    if (wave_active) {
+    // Every wave computes (a wave without valid heads works on zero queries
+    // and stores nothing): a branch around the MFMAs would make the compiler
+    // shuttle the accumulators between register files.
+    {
       f32x4 sacc[2] = {f32x4{}, f32x4{}};
       const char* kp = st + koff;
 #pragma unroll
       for (int s = 0; s < MLA_DQ / 32; ++s) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = lds16(kp + 2048 * s + 256 * kb);
+          const u32x4 a = lds16(kp + 512 * s + 18432 * kb);
           sacc[kb] = T::mma16(a, qf[s], sacc[kb]);
         }
       }
@@ -184,7 +190,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
         const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * sl2);
         l_run *= alpha;
 #pragma unroll
-        for (int db = 0; db < MLA_DV / 16; ++db) oacc[db] *= alpha;
+        for (int db = 0; db < MLA_DV / 16; ++db) acc_scale(oacc[db], alpha);
         m_run = m_new;
       }
       const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
@@ -198,11 +204,13 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
         }
       const u32x4 pb{T::pack2(pv[0][0], pv[0][1]), T::pack2(pv[0][2], pv[0][3]),
                      T::pack2(pv[1][0], pv[1][1]), T::pack2(pv[1][2], pv[1][3])};
-      const char* vp = st + toff;
+      const char* vpE = st + toffE;
+      const char* vpO = st + toffO;
 #pragma unroll
       for (int db = 0; db < MLA_DV / 16; ++db) {
-        const u32x2 r0 = lds_read_tr16(vp + 1024 * db);
-        const u32x2 r1 = lds_read_tr16(vp + 1024 * db + 256);
+        const char* vp = (db & 1) ? vpO : vpE;
+        const u32x2 r0 = lds_read_tr16(vp + 256 * db);
+        const u32x2 r1 = lds_read_tr16(vp + 256 * db + 18432);
         oacc[db] = T::mma16(u32x4{r0[0], r0[1], r1[0], r1[1]}, pb, oacc[db]);
       }
     }

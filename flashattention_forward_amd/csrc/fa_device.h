@@ -171,6 +171,37 @@ __device__ __forceinline__ u32x4 neg16x8(u32x4 v) {
   return v ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
 }
 
+// acc *= s for an MFMA accumulator that lives in AGPRs. Written as inline
+// assembly (read to a VGPR, multiply, write back) so that a rarely taken rescale
+// does not make the compiler keep the accumulators in VGPRs and copy them
+// around every MFMA.
+__device__ __forceinline__ void acc_scale(f32x4& acc, float s) {
+  float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
+  float t;
+  asm volatile(
+      "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
+      "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
+      "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
+      "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4\n\t"
+      "s_nop 2"
+      : "+a"(a0), "+a"(a1), "+a"(a2), "+a"(a3), "=&v"(t)
+      : "v"(s));
+  acc = f32x4{a0, a1, a2, a3};
+}
+
+// LDS tile layout shared by the direct-to-LDS copies: a tile of 16-byte chunks
+// (row r = key or token, chunk c) is cut into 8 x 8 blocks, one block per copy
+// instruction (8 rows x 128 contiguous bytes of global memory). Inside block
+// (RB = r >> 3, CB = c >> 3) the chunk sits at slot
+//     8 * (g ^ (RB & 1)) + (rho ^ 4 * ((g >> 1) & 1)),   g = c & 7, rho = r & 7,
+// which spreads both MFMA operand read patterns over all 64 banks: 16
+// consecutive rows of one chunk (ds_read_b128 key reads), and 4 or 8 rows of
+// 2 or 4 adjacent chunks (ds_read_b64_tr_b16 value reads).
+__device__ __forceinline__ int blk_slot(int r, int c) {
+  const int g = c & 7;
+  return 8 * (g ^ ((r >> 3) & 1)) + ((r & 7) ^ (4 * ((g >> 1) & 1)));
+}
+
 // Online-softmax rescale threshold in log2 units: the running max is moved
 // only when a tile's max exceeds it by more than this, so probabilities stay
 // <= 2^8 and the O rescale (a pass over all accumulators) is rare.

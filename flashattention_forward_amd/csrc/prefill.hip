@@ -19,10 +19,10 @@
 //  * K and V tiles go from global memory straight into LDS (global_load_lds,
 //    no register staging) into a ring of stages: the copy of tile t+1 is in
 //    flight while tile t is computed, and barriers wait on LDS traffic only;
-//  * tiles are stored chunk-major (16-byte chunk c of key row r at slot
-//    64 * c + r, V rows XOR-ed with 4 * (c & 3)), so a copy instruction is one
-//    chunk column of all 64 keys, and the K reads (16 rows of one chunk) and the
-//    transposed V reads (4 rows x 4 chunks) each touch distinct banks;
+//  * tiles are stored in 8 x 8 blocks of 16-byte chunks (blk_slot): a copy
+//    instruction moves 8 key rows x 128 contiguous bytes, and the K reads (16
+//    rows of one chunk) and the transposed V reads (4 rows x 4 chunks) each
+//    touch 64 distinct banks;
 //  * causal (bottom-right aligned) blocks stop at their last visible tile, waves
 //    skip tiles that none of their rows can see, and only tiles crossing the
 //    diagonal or the end of the keys are masked;
@@ -38,6 +38,7 @@ namespace fa {
 
 template <int D> struct PfCfg {
   static constexpr int NCH = D / 8;                 // 16-byte chunks per key row
+  static constexpr int NCB = NCH / 8;               // 8-chunk blocks per key row
   static constexpr int TILE = PF_BN * D * 2;        // bytes of one K (or V) tile
   static constexpr int STAGE = 2 * TILE;            // K tile then V tile
   static constexpr int NST = D == 64 ? 4 : 2;       // stages in the LDS ring
@@ -97,26 +98,26 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
   }
 
-  // Copies of tile t into stage (t - t_begin) % NST. Wave w fills chunk columns
-  // n = CPW * w .. + CPW - 1 of K and of V; lane l copies key row l of K and key
-  // row l ^ 4 * (n & 3) of V (the V swizzle). Keys past the end are clamped to
-  // the last key: their scores are masked and their probabilities are 0.
+  // Copies of tile t into stage (t - t_begin) % NST: the K and the V tile are
+  // each 8 * NCB blocks; wave w copies blocks n = 2 NCB w + i (i < 2 NCB) of
+  // both, i.e. key rows 16w .. 16w + 15. Lane l copies chunk
+  // 8 CB + ((l >> 3) ^ (RB & 1)) of key row 8 RB + ((l & 7) ^ 4 * ((l >> 4) & 1))
+  // (the inverse of blk_slot). Keys past the end are clamped to the last key:
+  // their scores are masked and their probabilities are 0.
   const uint32_t smem_lds = lds_addr(smem);
+  const int dma_rho = (lane & 7) ^ (4 * ((lane >> 4) & 1));
   auto issue = [&](int t) {
     const uint32_t st = smem_lds + ((t - t_begin) % C::NST) * C::STAGE;
     const int k0 = t * PF_BN;
-    const int kr = min(k0 + lane, p.Skv - 1);
-    const char* ksrc = kbase + (int64_t)kr * row_bytes + C::CPW * w * 16;
 #pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      const int n = C::CPW * w + i;
-      dma16(ksrc + 16 * i, st + n * 1024);
-    }
-#pragma unroll
-    for (int i = 0; i < C::CPW; ++i) {
-      const int n = C::CPW * w + i;
-      const int vr = min(k0 + (lane ^ (4 * (n & 3))), p.Skv - 1);
-      dma16(vbase + (int64_t)vr * row_bytes + n * 16, st + C::TILE + n * 1024);
+    for (int i = 0; i < 2 * C::NCB; ++i) {
+      const int n = 2 * C::NCB * w + i;
+      const int rb_odd = (i / C::NCB) & 1, cb = i % C::NCB;
+      const int key = min(k0 + 16 * w + 8 * rb_odd + dma_rho, p.Skv - 1);
+      const int chunk = 8 * cb + ((lane >> 3) ^ rb_odd);
+      const int64_t off = (int64_t)key * row_bytes + chunk * 16;
+      dma16(kbase + off, st + n * 1024);
+      dma16(vbase + off, st + C::TILE + n * 1024);
     }
   };
 
@@ -127,15 +128,16 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const float sl2 = p.scale_log2;
   const int q_last_wave = min(qw0 + 31, p.Sq - 1);
 
-  // Per-lane LDS offsets. K (A operand): row 32 * kb + c, chunk 2s + h.
-  const int koff = 1024 * h + 16 * c;
+  // Per-lane LDS offsets (blk_slot written out). K (A operand): row 32 kb + c,
+  // chunk 2s + h; the offset alternates with the parity of s.
+  const int kbase_off = 1024 * C::NCB * (c >> 3) + 128 * (h ^ ((c >> 3) & 1));
+  const int koffE = kbase_off + 16 * (c & 7), koffO = kbase_off + 16 * ((c & 7) ^ 4);
   // V^T (A operand) by transpose reads: lane j = lane & 15 of 16-lane group gb
-  // = (lane >> 4) & 1 reads rows 16 jj + 4h + j/4 (then + 8) of chunk
-  // 4 db + 2 gb + e, e = (j & 3) >> 1, byte 8 * (j & 1); rows are XOR-ed with
-  // 4 * (chunk & 3) = 8 gb + 4 e.
+  // = (lane >> 4) & 1 reads rows 16 jj + 4h + j/4 (read A) and + 8 (read B) of
+  // chunk 4 db + 2 gb + e, e = (j & 3) >> 1, byte 8 * (j & 1).
   const int j = lane & 15, gb = (lane >> 4) & 1, e = (j & 3) >> 1;
-  const int voffA = 1024 * (2 * gb + e) + 128 * gb + 64 * (h ^ e) + 16 * (j >> 2) + 8 * (j & 1);
-  const int voffB = voffA + 128 - 256 * gb;
+  const int voffA = 256 * gb + 128 * e + 64 * (h ^ gb) + 16 * (j >> 2) + 8 * (j & 1);
+  const int voffB = voffA + 1024 * C::NCB + 128 * (1 - 2 * e);
 
   for (int t = t_begin; t < min(t_end, t_begin + C::NST - 1); ++t) issue(t);
 
@@ -160,7 +162,7 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = lds16(Ks + koff + 2048 * s + 512 * kb);
+          const u32x4 a = lds16(Ks + ((s & 1) ? koffO : koffE) + 256 * s + 4096 * C::NCB * kb);
           sacc[kb] = T::mma32(a, qf[s], sacc[kb]);
         }
       }
@@ -216,8 +218,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       for (int jj = 0; jj < 4; ++jj) {
 #pragma unroll
         for (int db = 0; db < D / 32; ++db) {
-          const u32x2 ra = lds_read_tr16(Vs + voffA + 4096 * db + 256 * jj);
-          const u32x2 rb = lds_read_tr16(Vs + voffB + 4096 * db + 256 * jj);
+          const u32x2 ra = lds_read_tr16(Vs + voffA + 2048 * C::NCB * jj + 512 * db);
+          const u32x2 rb = lds_read_tr16(Vs + voffB + 2048 * C::NCB * jj + 512 * db);
           oacc[db] = T::mma32(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb[jj], oacc[db]);
         }
       }
