@@ -35,6 +35,12 @@ template <> struct in_traits<bf16_t> {
     bf16x2 v = {(__bf16)a, (__bf16)b};
     return __builtin_bit_cast(uint32_t, v);
   }
+  // c + the two 16-bit values packed in p (v_dot2c_f32_bf16 with (1, 1)).
+  static __device__ __forceinline__ float sum2(uint32_t p, float c) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, p),
+                                           bf16x2{(__bf16)1.0f, (__bf16)1.0f}, c, false);
+  }
   static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -50,6 +56,11 @@ template <> struct in_traits<f16_t> {
     typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     f16x2 v = {(_Float16)a, (_Float16)b};
     return __builtin_bit_cast(uint32_t, v);
+  }
+  static __device__ __forceinline__ float sum2(uint32_t p, float c) {
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, p),
+                                  f16x2{(_Float16)1.0f, (_Float16)1.0f}, c, false);
   }
   static __device__ __forceinline__ f32x16 mma32(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
@@ -163,7 +174,34 @@ __device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
       : "memory");
 }
 
+// Same copy with a wave-uniform 64-bit base (SGPRs) and a per-lane 32-bit
+// byte offset: no per-lane 64-bit address arithmetic at all.
+__device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
+  uint32_t saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\t"
+      "s_mov_b32 m0, %3\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\t"
+      "s_mov_b32 m0, %0"
+      : "=&s"(saved)
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_base))
+      : "memory");
+}
+
 __device__ __forceinline__ u32x4 lds16(const char* p) { return *(const u32x4*)p; }
+
+// max / sum of a value over lanes l and l ^ 32 (v_permlane32_swap, no LDS).
+__device__ __forceinline__ float max_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor32(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 // Flip the sign of the 8 bf16/fp16 values of a fragment (a negative scale is
 // applied as |scale| on -Q so the running max stays a max).

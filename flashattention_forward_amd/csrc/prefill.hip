@@ -17,8 +17,13 @@
 //    is relabelled to match the accumulator layout; the V^T operand comes from
 //    the row-major V tile through the LDS transpose read (ds_read_b64_tr_b16);
 //  * K and V tiles go from global memory straight into LDS (global_load_lds,
-//    no register staging) into a ring of stages: the copy of tile t+1 is in
-//    flight while tile t is computed, and barriers wait on LDS traffic only;
+//    no register staging), each into a 2-stage ring, and barriers wait on LDS
+//    traffic only;
+//  * the steps are software-pipelined as in the FlashAttention-3 schedule that
+//    "perf: FlashAttention-3 style MLA PageAttention" (FlashInfer, change list
+//    item 3) adopts: the MFMAs of S(t+1) = K(t+1) Q^T are issued before the
+//    softmax of tile t, so the exp-heavy vector work of one tile overlaps the
+//    matrix-core work of the next;
 //  * tiles are stored in 8 x 8 blocks of 16-byte chunks (blk_slot): a copy
 //    instruction moves 8 key rows x 128 contiguous bytes, and the K reads (16
 //    rows of one chunk) and the transposed V reads (4 rows x 4 chunks) each
@@ -31,26 +36,25 @@
 //    accumulators are rarely rescaled;
 //  * a workgroup may process one of several key splits; it then writes its
 //    normalised partial O and log-sum-exp for a separate combine kernel.
+#include <type_traits>
+
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
 template <int D> struct PfCfg {
-  static constexpr int NCH = D / 8;                 // 16-byte chunks per key row
-  static constexpr int NCB = NCH / 8;               // 8-chunk blocks per key row
-  static constexpr int TILE = PF_BN * D * 2;        // bytes of one K (or V) tile
-  static constexpr int STAGE = 2 * TILE;            // K tile then V tile
-  static constexpr int NST = D == 64 ? 4 : 2;       // stages in the LDS ring
-  static constexpr int CPW = NCH / 4;               // chunk columns per wave (K and V each)
-  static constexpr int IPW = 2 * CPW;               // copy instructions per wave and tile
+  static constexpr int NCH = D / 8;           // 16-byte chunks per key row
+  static constexpr int NCB = NCH / 8;         // 8-chunk blocks per key row
+  static constexpr int TILE = PF_BN * D * 2;  // bytes of one K (or V) tile
+  static constexpr int LDS = 4 * TILE;        // 2 K stages + 2 V stages
 };
 
 template <int D, typename TI, typename TO, bool CAUSAL>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   using C = PfCfg<D>;
   using T = in_traits<TI>;
-  __shared__ __attribute__((aligned(16))) char smem[C::NST * C::STAGE];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int c = lane & 31, h = lane >> 5;
@@ -98,28 +102,42 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
   }
 
-  // Copies of tile t into stage (t - t_begin) % NST: the K and the V tile are
-  // each 8 * NCB blocks; wave w copies blocks n = 2 NCB w + i (i < 2 NCB) of
-  // both, i.e. key rows 16w .. 16w + 15. Lane l copies chunk
-  // 8 CB + ((l >> 3) ^ (RB & 1)) of key row 8 RB + ((l & 7) ^ 4 * ((l >> 4) & 1))
-  // (the inverse of blk_slot). Keys past the end are clamped to the last key:
+  // Copies. K and V have separate 2-stage rings: K tile t lives in K stage
+  // (t - t_begin) & 1, V tile t in V stage (t - t_begin) & 1. Each tile is
+  // 8 * NCB blocks; wave w copies blocks n = 2 NCB w + i (i < 2 NCB), i.e. key
+  // rows 16w .. 16w + 15. Lane l copies chunk 8 CB + ((l >> 3) ^ (RB & 1)) of
+  // key row 8 RB + ((l & 7) ^ 4 * ((l >> 4) & 1)) (the inverse of blk_slot).
+  // The per-lane byte offsets are fixed; a tile only moves the wave-uniform
+  // base. In the last tile, keys past the end are clamped to the last key:
   // their scores are masked and their probabilities are 0.
   const uint32_t smem_lds = lds_addr(smem);
   const int dma_rho = (lane & 7) ^ (4 * ((lane >> 4) & 1));
-  auto issue = [&](int t) {
-    const uint32_t st = smem_lds + ((t - t_begin) % C::NST) * C::STAGE;
+  uint32_t voff[2 * C::NCB];
+  int vrow[2 * C::NCB];
+#pragma unroll
+  for (int i = 0; i < 2 * C::NCB; ++i) {
+    const int rb_odd = (i / C::NCB) & 1, cb = i % C::NCB;
+    vrow[i] = 16 * w + 8 * rb_odd + dma_rho;
+    voff[i] = (uint32_t)(vrow[i] * row_bytes + (8 * cb + ((lane >> 3) ^ rb_odd)) * 16);
+  }
+  auto issue = [&](const char* base, uint32_t st, int t) {
     const int k0 = t * PF_BN;
+    const char* src = base + (int64_t)k0 * row_bytes;
+    const bool tail = k0 + PF_BN > p.Skv;
 #pragma unroll
     for (int i = 0; i < 2 * C::NCB; ++i) {
-      const int n = 2 * C::NCB * w + i;
-      const int rb_odd = (i / C::NCB) & 1, cb = i % C::NCB;
-      const int key = min(k0 + 16 * w + 8 * rb_odd + dma_rho, p.Skv - 1);
-      const int chunk = 8 * cb + ((lane >> 3) ^ rb_odd);
-      const int64_t off = (int64_t)key * row_bytes + chunk * 16;
-      dma16(kbase + off, st + n * 1024);
-      dma16(vbase + off, st + C::TILE + n * 1024);
+      uint32_t o = voff[i];
+      if (tail) {
+        const int over = vrow[i] - (p.Skv - 1 - k0);
+        if (over > 0) o -= (uint32_t)(over * row_bytes);
+      }
+      dma16s(src, o, st + (2 * C::NCB * w + i) * 1024);
     }
   };
+  auto k_stage = [&](int t) { return ((t - t_begin) & 1) * C::TILE; };
+  auto v_stage = [&](int t) { return (2 + ((t - t_begin) & 1)) * C::TILE; };
+  auto issue_k = [&](int t) { issue(kbase, smem_lds + k_stage(t), t); };
+  auto issue_v = [&](int t) { issue(vbase, smem_lds + v_stage(t), t); };
 
   f32x16 oacc[D / 32];
 #pragma unroll
@@ -139,95 +157,123 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   const int voffA = 256 * gb + 128 * e + 64 * (h ^ gb) + 16 * (j >> 2) + 8 * (j & 1);
   const int voffB = voffA + 1024 * C::NCB + 128 * (1 - 2 * e);
 
-  for (int t = t_begin; t < min(t_end, t_begin + C::NST - 1); ++t) issue(t);
-
-  for (int t = t_begin; t < t_end; ++t) {
-    // Wait for this wave's copies of tile t (later tiles may stay in flight).
-    if (C::NST >= 4 && t + 2 < t_end)
-      wait_vmcnt<2 * C::IPW>();
-    else if (C::NST >= 3 && t + 1 < t_end)
-      wait_vmcnt<C::IPW>();
-    else
-      wait_vmcnt<0>();
-    lds_barrier();
-    if (t + C::NST - 1 < t_end) issue(t + C::NST - 1);
-
-    const int k0 = t * PF_BN;
-    const bool active = !CAUSAL || k0 <= q_last_wave + off;
-    if (active) {
-      const char* Ks = smem + ((t - t_begin) % C::NST) * C::STAGE;
-      const char* Vs = Ks + C::TILE;
-      f32x16 sacc[2] = {f32x16{}, f32x16{}};
+  // S^T of one tile: 2 * D / 16 MFMAs from the K stage.
+  auto qk = [&](f32x16 (&sacc)[2], const char* Ks) {
+    sacc[0] = f32x16{};
+    sacc[1] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < D / 16; ++s) {
+    for (int s = 0; s < D / 16; ++s) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const u32x4 a = lds16(Ks + ((s & 1) ? koffO : koffE) + 256 * s + 4096 * C::NCB * kb);
-          sacc[kb] = T::mma32(a, qf[s], sacc[kb]);
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 a = lds16(Ks + ((s & 1) ? koffO : koffE) + 256 * s + 4096 * C::NCB * kb);
+        sacc[kb] = T::mma32(a, qf[s], sacc[kb]);
       }
-      const bool need_mask = (k0 + PF_BN > p.Skv) || (CAUSAL && k0 + PF_BN - 1 > qw0 + off);
-      // Masked keys: -inf for the max, probability forced to 0 below.
-      const int lim = !need_mask ? k0 + PF_BN : (CAUSAL ? min(p.Skv - 1, qi + off) : p.Skv - 1);
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key > lim) sacc[kb][i] = -INFINITY;
-          }
-      }
-      float mx = sacc[0][0];
+    }
+  };
+
+  // Online softmax of one tile's scores, then O^T += V^T P^T. MASK: keys beyond
+  // `lim` (per lane) are excluded; the unmasked body carries no index arithmetic.
+  auto softmax_pv = [&](auto mask_tag, f32x16 (&sacc)[2], const char* Vs, int k0, int lim) {
+    constexpr bool MASK = decltype(mask_tag)::value;
+    if constexpr (MASK) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-      mx = fmaxf(mx, xor32(mx));
-      // Lazy rescale: move the running max only when it grows by > 2^8.
-      const bool grow =
-          mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
-      if (__ballot(grow)) {
-        const float m_new = grow ? mx : m_run;
-        const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * sl2);
-        l_run *= alpha;
-#pragma unroll
-        for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
-        m_run = m_new;
-      }
-      const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
-      u32x4 pb[4];
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int kb = jj >> 1, base = 8 * (jj & 1);
-        float pv[8];
-#pragma unroll
-        for (int ee = 0; ee < 8; ++ee) {
-          pv[ee] = fast_exp2(fmaf(sacc[kb][base + ee], sl2, nb));
-          if (need_mask) {
-            const int i = base + ee;
-            const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-            if (key > lim) pv[ee] = 0.f;
-          }
-          l_run += pv[ee];
+        for (int i = 0; i < 16; ++i) {
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key > lim) sacc[kb][i] = -INFINITY;
         }
-        pb[jj] = u32x4{T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
-                       T::pack2(pv[6], pv[7])};
-      }
+    }
+    float mx = sacc[0][0];
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int db = 0; db < D / 32; ++db) {
-          const u32x2 ra = lds_read_tr16(Vs + voffA + 2048 * C::NCB * jj + 512 * db);
-          const u32x2 rb = lds_read_tr16(Vs + voffB + 2048 * C::NCB * jj + 512 * db);
-          oacc[db] = T::mma32(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb[jj], oacc[db]);
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
+    mx = max_xor32(mx);
+    // Lazy rescale: move the running max only when it grows by > 2^8.
+    const bool grow = mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
+    if (__ballot(grow)) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * sl2);
+      l_run *= alpha;
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
+      m_run = m_new;
+    }
+    const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
+    u32x4 pb[4];
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int kb = jj >> 1, base = 8 * (jj & 1);
+      float pv[8];
+#pragma unroll
+      for (int ee = 0; ee < 8; ++ee) {
+        pv[ee] = fast_exp2(fmaf(sacc[kb][base + ee], sl2, nb));
+        if constexpr (MASK) {
+          const int i = base + ee;
+          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+          if (key > lim) pv[ee] = 0.f;
         }
+      }
+      pb[jj] = u32x4{T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
+                     T::pack2(pv[6], pv[7])};
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4) l_run = T::sum2(pb[jj][q4], l_run);
+    }
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+#pragma unroll
+      for (int db = 0; db < D / 32; ++db) {
+        const u32x2 ra = lds_read_tr16(Vs + voffA + 2048 * C::NCB * jj + 512 * db);
+        const u32x2 rb = lds_read_tr16(Vs + voffB + 2048 * C::NCB * jj + 512 * db);
+        oacc[db] = T::mma32(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb[jj], oacc[db]);
       }
     }
+  };
+
+  // Tiles [t_begin, t_mask) are visible to every row of the workgroup and lie
+  // inside the keys; the rest (the causal diagonal, the key tail) are masked.
+  int t_mask = p.Skv / PF_BN;
+  if (CAUSAL)
+    t_mask = min(t_mask, q0 + off - (PF_BN - 1) >= 0 ? (q0 + off - (PF_BN - 1)) / PF_BN + 1 : 0);
+  t_mask = max(t_begin, min(t_mask, t_end));
+  const int lim = CAUSAL ? min(p.Skv - 1, qi + off) : p.Skv - 1;
+
+  // Software pipeline (the scores of tile t+1 are computed on the matrix cores
+  // while the softmax of tile t runs on the vector ALUs):
+  //   prologue: K(t0); wait; S(t0) = QK(t0); copy V(t0), K(t0+1)
+  //   step t:   wait for K(t+1), V(t); copy K(t+2), V(t+1);
+  //             S(t+1) = QK(t+1); softmax(S(t)); O += P V(t)
+  // One barrier per step also guarantees that the stages being refilled
+  // (K(t), V(t-1)) have been read by every wave.
+  f32x16 s_cur[2], s_nxt[2];
+  if (t_begin < t_end) {
+    issue_k(t_begin);
+    wait_vmcnt<0>();
+    lds_barrier();
+    qk(s_cur, smem + k_stage(t_begin));
+    issue_v(t_begin);
+    if (t_begin + 1 < t_end) issue_k(t_begin + 1);
   }
+  auto step = [&](auto mask_tag, int t) {
+    wait_vmcnt<0>();
+    lds_barrier();
+    if (t + 2 < t_end) issue_k(t + 2);
+    if (t + 1 < t_end) {
+      issue_v(t + 1);
+      qk(s_nxt, smem + k_stage(t + 1));
+    }
+    const int k0 = t * PF_BN;
+    if (!decltype(mask_tag)::value || !CAUSAL || k0 <= q_last_wave + off)
+      softmax_pv(mask_tag, s_cur, smem + v_stage(t), k0, lim);
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+  };
+  for (int t = t_begin; t < t_mask; ++t) step(std::integral_constant<bool, false>{}, t);
+  for (int t = t_mask; t < t_end; ++t) step(std::integral_constant<bool, true>{}, t);
 
   // Epilogue: both lane halves hold parts of the row sum.
-  const float l_tot = l_run + xor32(l_run);
+  const float l_tot = sum_xor32(l_run);
   if (!q_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
