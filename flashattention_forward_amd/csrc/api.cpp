@@ -56,7 +56,7 @@ struct PrefillPlan {
 
 PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split) {
   PrefillPlan pl;
-  pl.n_qtiles = ceil_div(Sq, PF_BM);
+  pl.n_qtiles = ceil_div(Sq, pf_bm(D));
   const int64_t base = (int64_t)B * Hq * pl.n_qtiles;
   const int max_tiles = ceil_div(Skv, PF_BN);
   int S = 1;
@@ -65,9 +65,9 @@ PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split
     if (forced > 0) {
       S = std::min(forced, 64);
     } else {
-      // Two 4-wave workgroups per CU keep two waves on every SIMD; split the
-      // keys only while each split keeps at least 8 tiles (512 keys).
-      const int64_t target = 2 * (int64_t)planner_cus();
+      // Two waves on every SIMD: two 4-wave or one 8-wave workgroup per CU.
+      // Split the keys only while each split keeps at least 8 tiles (512 keys).
+      const int64_t target = (8 / pf_waves(D)) * (int64_t)planner_cus();
       while (base * S < target && S < 16 && max_tiles / (2 * S) >= 8) S *= 2;
     }
     S = std::max(1, std::min(S, std::max(1, max_tiles)));
@@ -139,7 +139,7 @@ int check_prefill(const void* q, const void* k, const void* v, void* o, const fl
   if ((q && !aligned16(q)) || (k && !aligned16(k)) || (v && !aligned16(v)) ||
       (o && !aligned16(o)) || (lse && !aligned4(lse)))
     return FA_ERR_ALIGN;
-  if ((int64_t)B * Hq * ceil_div(Sq, PF_BM) > kMaxGrid) return FA_ERR_SHAPE;
+  if ((int64_t)B * Hq * ceil_div(Sq, PF_BM_MIN) > kMaxGrid) return FA_ERR_SHAPE;
   return FA_OK;
 }
 
@@ -197,7 +197,9 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   p.n_splits = pl.n_splits;
   p.q_neg = scale < 0.f;
   p.scale = std::fabs(scale);
-  p.scale_log2 = p.scale * 1.4426950408889634f;
+  // Exponent scale; zero is passed as the smallest positive value so that
+  // masked scores (-inf) still give probability 0 (and exp2(s * 1e-30) == 1).
+  p.scale_log2 = std::max(p.scale * 1.4426950408889634f, 1e-30f);
   const int64_t rows = (int64_t)B * Sq * Hq;
   if (pl.n_splits > 1) {
     p.part_o = (float*)workspace;

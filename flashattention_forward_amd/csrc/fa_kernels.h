@@ -20,7 +20,7 @@ struct PrefillParams {
   float* part_o;    // [S, B, Sq, Hq, D] fp32 when n_splits > 1
   float* part_lse;  // [S, B, Sq, Hq]
   int B, Hq, Hkv, Sq, Skv;
-  int n_qtiles;  // ceil(Sq / 128)
+  int n_qtiles;  // ceil(Sq / pf_bm(D))
   int n_splits;  // key splits per query tile
   int q_neg;     // 1: the scale was negative; the kernel uses -Q and |scale|
   float scale;       // |scale|, multiplies q.k
@@ -81,7 +81,12 @@ hipError_t launch_decode_mla(const DecodeMlaParams& p, InType it, hipStream_t st
 hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream);
 
 // Tile constants the host planner needs.
-constexpr int PF_BM = 128;  // query rows per prefill workgroup (4 waves x 32)
+// Prefill: waves per workgroup (each wave owns 32 query rows). Head size 128
+// runs one 8-wave workgroup per CU: every K/V tile copied into LDS then serves
+// 256 query rows, which halves the L2-to-CU traffic per flop.
+constexpr int pf_waves(int D) { return D == 128 ? 8 : 4; }
+constexpr int pf_bm(int D) { return 32 * pf_waves(D); }  // query rows per workgroup
+constexpr int PF_BM_MIN = 128;
 constexpr int PF_BN = 64;   // keys per prefill tile
 constexpr int DEC_TILE = 32;  // tokens per decode tile
 constexpr int MLA_HEADS_PER_WG = 64;

@@ -48,15 +48,19 @@ template <int D> struct PfCfg {
   static constexpr int NCB = NCH / 8;         // 8-chunk blocks per key row
   static constexpr int TILE = PF_BN * D * 2;  // bytes of one K (or V) tile
   static constexpr int LDS = 4 * TILE;        // 2 K stages + 2 V stages
+  static constexpr int NW = pf_waves(D);      // waves per workgroup
+  static constexpr int BM = 32 * NW;          // query rows per workgroup
+  static constexpr int BPW = 8 * NCB / NW;    // 1 KB blocks of a tile each wave copies
 };
 
 template <int D, typename TI, typename TO, bool CAUSAL>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
+__global__ __launch_bounds__(64 * pf_waves(D), 2) void prefill_kernel(PrefillParams p) {
   using C = PfCfg<D>;
   using T = in_traits<TI>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int c = lane & 31, h = lane >> 5;
 
   // Logical block: (b, kv head g, query tile, head in group, split), with the
@@ -75,10 +79,10 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   if (CAUSAL) qt = p.n_qtiles - 1 - qt;  // longest rows first
   const int hq = g * G + hh;
   const int off = p.Skv - p.Sq;  // bottom-right alignment
-  const int q0 = qt * PF_BM;
+  const int q0 = qt * C::BM;
 
   int kv_end = p.Skv;
-  if (CAUSAL) kv_end = min(kv_end, min(q0 + PF_BM, p.Sq) + off);
+  if (CAUSAL) kv_end = min(kv_end, min(q0 + C::BM, p.Sq) + off);
   const int n_tiles = kv_end > 0 ? (kv_end + PF_BN - 1) / PF_BN : 0;
   const int tps = (n_tiles + S - 1) / S;
   const int t_begin = min(split * tps, n_tiles);
@@ -104,34 +108,38 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
 
   // Copies. K and V have separate 2-stage rings: K tile t lives in K stage
   // (t - t_begin) & 1, V tile t in V stage (t - t_begin) & 1. Each tile is
-  // 8 * NCB blocks; wave w copies blocks n = 2 NCB w + i (i < 2 NCB), i.e. key
-  // rows 16w .. 16w + 15. Lane l copies chunk 8 CB + ((l >> 3) ^ (RB & 1)) of
-  // key row 8 RB + ((l & 7) ^ 4 * ((l >> 4) & 1)) (the inverse of blk_slot).
-  // The per-lane byte offsets are fixed; a tile only moves the wave-uniform
-  // base. In the last tile, keys past the end are clamped to the last key:
-  // their scores are masked and their probabilities are 0.
-  const uint32_t smem_lds = lds_addr(smem);
+  // 8 * NCB blocks of 1 KB (8 key rows x 8 chunks); wave w copies blocks
+  // n = BPW w + i (i < BPW). In block n (row block RB = n / NCB, chunk block
+  // CB = n % NCB) lane l copies chunk 8 CB + ((l >> 3) ^ (RB & 1)) of key row
+  // 8 RB + ((l & 7) ^ 4 * ((l >> 4) & 1)) (the inverse of blk_slot), so a
+  // copy instruction moves 8 rows x 128 contiguous bytes. The per-lane byte
+  // offsets are fixed; a tile only moves the wave-uniform base. In the last
+  // tile, keys past the end are clamped to the last key: their scores are
+  // masked and their probabilities are 0.
+  const uint32_t smem_lds = __builtin_amdgcn_readfirstlane(lds_addr(smem));
   const int dma_rho = (lane & 7) ^ (4 * ((lane >> 4) & 1));
-  uint32_t voff[2 * C::NCB];
-  int vrow[2 * C::NCB];
+  uint32_t voff[C::BPW];
+  int vrow[C::BPW];
 #pragma unroll
-  for (int i = 0; i < 2 * C::NCB; ++i) {
-    const int rb_odd = (i / C::NCB) & 1, cb = i % C::NCB;
-    vrow[i] = 16 * w + 8 * rb_odd + dma_rho;
+  for (int i = 0; i < C::BPW; ++i) {
+    const int n = C::BPW * w + i, RB = n / C::NCB, cb = n % C::NCB, rb_odd = RB & 1;
+    vrow[i] = 8 * RB + dma_rho;
     voff[i] = (uint32_t)(vrow[i] * row_bytes + (8 * cb + ((lane >> 3) ^ rb_odd)) * 16);
   }
   auto issue = [&](const char* base, uint32_t st, int t) {
     const int k0 = t * PF_BN;
     const char* src = base + (int64_t)k0 * row_bytes;
-    const bool tail = k0 + PF_BN > p.Skv;
+    const uint32_t dst = st + C::BPW * w * 1024;
+    if (k0 + PF_BN <= p.Skv) {
 #pragma unroll
-    for (int i = 0; i < 2 * C::NCB; ++i) {
-      uint32_t o = voff[i];
-      if (tail) {
-        const int over = vrow[i] - (p.Skv - 1 - k0);
-        if (over > 0) o -= (uint32_t)(over * row_bytes);
+      for (int i = 0; i < C::BPW; ++i) dma16s(src, voff[i], dst + i * 1024);
+    } else {
+      const int last = p.Skv - 1 - k0;
+#pragma unroll
+      for (int i = 0; i < C::BPW; ++i) {
+        const int over = vrow[i] - last;
+        dma16s(src, over > 0 ? voff[i] - (uint32_t)(over * row_bytes) : voff[i], dst + i * 1024);
       }
-      dma16s(src, o, st + (2 * C::NCB * w + i) * 1024);
     }
   };
   auto k_stage = [&](int t) { return ((t - t_begin) & 1) * C::TILE; };
@@ -171,26 +179,33 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
     }
   };
 
-  // Online softmax of one tile's scores, then O^T += V^T P^T. MASK: keys beyond
-  // `lim` (per lane) are excluded; the unmasked body carries no index arithmetic.
-  auto softmax_pv = [&](auto mask_tag, f32x16 (&sacc)[2], const char* Vs, int k0, int lim) {
-    constexpr bool MASK = decltype(mask_tag)::value;
-    if constexpr (MASK) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > lim) sacc[kb][i] = -INFINITY;
-        }
-    }
+  // Last key this lane's query row may see.
+  const int lim = CAUSAL ? min(p.Skv - 1, qi + off) : p.Skv - 1;
+
+  // Row max of one tile's scores (both lane halves combined).
+  auto tile_max = [&](const f32x16 (&sacc)[2]) {
     float mx = sacc[0][0];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sacc[kb][i]);
-    mx = max_xor32(mx);
-    // Lazy rescale: move the running max only when it grows by > 2^8.
+    return max_xor32(mx);
+  };
+  // Masked tiles: keys beyond `lim` (per lane) get score -inf, and the max is
+  // taken again over what is left.
+  auto apply_mask = [&](f32x16 (&sacc)[2], int k0) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
+        if (key > lim) sacc[kb][i] = -INFINITY;
+      }
+    return tile_max(sacc);
+  };
+  // Lazy rescale: the running max moves only when it grows by > 2^8; returns
+  // the exponent offset -m * scale * log2(e).
+  auto rescale = [&](float mx) {
     const bool grow = mx > m_run && (m_run == -INFINITY || (mx - m_run) * sl2 > RESCALE_LOG2);
     if (__ballot(grow)) {
       const float m_new = grow ? mx : m_run;
@@ -200,35 +215,86 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
-    const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
+    return m_run == -INFINITY ? 0.f : -m_run * sl2;
+  };
+
+  // One straight-line block, written out in issue order and fenced slot by
+  // slot so that the compiler keeps the interleave:
+  //   slots 0 .. NQK-1: one MFMA of S(t+1) = K(t+1) Q^T, the K read PD MFMAs
+  //     ahead, and VPS vector ops that turn S(t) into P(t) (exp2, bf16 pack,
+  //     row sums);
+  //   slots 0 .. NPV-1: one MFMA of O^T += V^T(t) P^T(t), its transpose reads
+  //     PD MFMAs ahead, and part of the row max of S(t+1) (returned in mx_next).
+  //   Masked scores are -inf already, and exp2(-inf * sl2 + nb) = 0 because
+  //   sl2 > 0 (a zero scale is passed as the smallest positive one).
+  auto body = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const char* Ks, const char* Vs, float nb,
+                  float& mx_next) {
+    constexpr int NQK = D / 8, NPV = D / 8, NDB = D / 32, PD = 4;
+    constexpr int OPE = 2;              // vector ops per probability
+    constexpr int OPJ = 8 * OPE + 8;    // per 8 probabilities: + 4 packs + 4 sums
+    constexpr int NOPS = 4 * OPJ;
+    constexpr int VPS = (NOPS + NQK - 1) / NQK;
+    float pv[32];
     u32x4 pb[4];
+    auto valu = [&](int k) {
+      const int jj = k / OPJ, r = k % OPJ, kb = jj >> 1, base = 8 * (jj & 1);
+      if (r < 8 * OPE) {
+        const int ee = r / OPE, ph = r % OPE, x = 8 * jj + ee;
+        if (ph == 0)
+          pv[x] = fmaf(cur[kb][base + ee], sl2, nb);
+        else
+          pv[x] = fast_exp2(pv[x]);
+      } else if (r < 8 * OPE + 4) {
+        const int q4 = r - 8 * OPE;
+        pb[jj][q4] = T::pack2(pv[8 * jj + 2 * q4], pv[8 * jj + 2 * q4 + 1]);
+      } else {
+        l_run = T::sum2(pb[jj][r - 8 * OPE - 4], l_run);
+      }
+    };
+    u32x4 kf[NQK];
+    u32x2 va[NPV], vb[NPV];
+    auto kread = [&](int i) {
+      const int s = i >> 1, kb = i & 1;
+      kf[i] = lds16(Ks + ((s & 1) ? koffO : koffE) + 256 * s + 4096 * C::NCB * kb);
+    };
+    auto vread = [&](int i) {
+      const int jj = i / NDB, db = i % NDB;
+      va[i] = lds_read_tr16(Vs + voffA + 2048 * C::NCB * jj + 512 * db);
+      vb[i] = lds_read_tr16(Vs + voffB + 2048 * C::NCB * jj + 512 * db);
+    };
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int kb = jj >> 1, base = 8 * (jj & 1);
-      float pv[8];
+    for (int i = 0; i < PD; ++i) kread(i);
 #pragma unroll
-      for (int ee = 0; ee < 8; ++ee) {
-        pv[ee] = fast_exp2(fmaf(sacc[kb][base + ee], sl2, nb));
-        if constexpr (MASK) {
-          const int i = base + ee;
-          const int key = k0 + 32 * kb + 8 * (i >> 2) + 4 * h + (i & 3);
-          if (key > lim) pv[ee] = 0.f;
+    for (int i = 0; i < NQK; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + PD < NQK) kread(i + PD);
+      else vread(i + PD - NQK);
+      const int s = i >> 1, kb = i & 1;
+      nxt[kb] = T::mma32(kf[i], qf[s], s == 0 ? f32x16{} : nxt[kb]);
+#pragma unroll
+      for (int v = 0; v < VPS; ++v)
+        if (i * VPS + v < NOPS) valu(i * VPS + v);
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < NPV; ++i) {
+      __builtin_amdgcn_sched_barrier(0);
+      if (i + PD < NPV) vread(i + PD);
+      const int jj = i / NDB, db = i % NDB;
+      oacc[db] = T::mma32(u32x4{va[i][0], va[i][1], vb[i][0], vb[i][1]}, pb[jj], oacc[db]);
+      // 32 scores, 4 per slot from slot 2 on (the score MFMAs have drained by then).
+      if (i >= 2) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int x = 4 * (i - 2) + u;
+          if (x < 32) mx = fmaxf(mx, nxt[x >> 4][x & 15]);
         }
       }
-      pb[jj] = u32x4{T::pack2(pv[0], pv[1]), T::pack2(pv[2], pv[3]), T::pack2(pv[4], pv[5]),
-                     T::pack2(pv[6], pv[7])};
-#pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) l_run = T::sum2(pb[jj][q4], l_run);
     }
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-#pragma unroll
-      for (int db = 0; db < D / 32; ++db) {
-        const u32x2 ra = lds_read_tr16(Vs + voffA + 2048 * C::NCB * jj + 512 * db);
-        const u32x2 rb = lds_read_tr16(Vs + voffB + 2048 * C::NCB * jj + 512 * db);
-        oacc[db] = T::mma32(u32x4{ra[0], ra[1], rb[0], rb[1]}, pb[jj], oacc[db]);
-      }
-    }
+    for (int x = 4 * (NPV - 2); x < 32; ++x) mx = fmaxf(mx, nxt[x >> 4][x & 15]);
+    mx_next = max_xor32(mx);
   };
 
   // Tiles [t_begin, t_mask) are visible to every row of the workgroup and lie
@@ -237,7 +303,6 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   if (CAUSAL)
     t_mask = min(t_mask, q0 + off - (PF_BN - 1) >= 0 ? (q0 + off - (PF_BN - 1)) / PF_BN + 1 : 0);
   t_mask = max(t_begin, min(t_mask, t_end));
-  const int lim = CAUSAL ? min(p.Skv - 1, qi + off) : p.Skv - 1;
 
   // Software pipeline (the scores of tile t+1 are computed on the matrix cores
   // while the softmax of tile t runs on the vector ALUs):
@@ -246,31 +311,52 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(PrefillParams p) {
   //             S(t+1) = QK(t+1); softmax(S(t)); O += P V(t)
   // One barrier per step also guarantees that the stages being refilled
   // (K(t), V(t-1)) have been read by every wave.
-  f32x16 s_cur[2], s_nxt[2];
+  // The scores alternate between two register sets (the unmasked loop is
+  // unrolled by two so that no copies are needed). mx_pend is the row max of
+  // the scores held for the next step, before any mask.
+  f32x16 sA[2], sB[2];
+  float mx_pend = -INFINITY;
   if (t_begin < t_end) {
     issue_k(t_begin);
     wait_vmcnt<0>();
     lds_barrier();
-    qk(s_cur, smem + k_stage(t_begin));
+    qk(sA, smem + k_stage(t_begin));
+    mx_pend = tile_max(sA);
     issue_v(t_begin);
     if (t_begin + 1 < t_end) issue_k(t_begin + 1);
   }
-  auto step = [&](auto mask_tag, int t) {
+  auto step = [&](auto mask_tag, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
+    constexpr bool MASK = decltype(mask_tag)::value;
     wait_vmcnt<0>();
     lds_barrier();
     if (t + 2 < t_end) issue_k(t + 2);
-    if (t + 1 < t_end) {
-      issue_v(t + 1);
-      qk(s_nxt, smem + k_stage(t + 1));
-    }
-    const int k0 = t * PF_BN;
-    if (!decltype(mask_tag)::value || !CAUSAL || k0 <= q_last_wave + off)
-      softmax_pv(mask_tag, s_cur, smem + v_stage(t), k0, lim);
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) s_cur[kb] = s_nxt[kb];
+    if (t + 1 < t_end) issue_v(t + 1);
+    // After the last tile the block still computes scores from a stale K stage
+    // (in bounds, never used): that keeps the block free of branches.
+    // A tile wholly above this wave's causal diagonal is masked out entirely
+    // (every probability 0); it runs through the same block.
+    const float mx = MASK ? apply_mask(cur, t * PF_BN) : mx_pend;
+    const float nb = rescale(mx);
+    body(cur, nxt, smem + k_stage(t + 1), smem + v_stage(t), nb, mx_pend);
   };
-  for (int t = t_begin; t < t_mask; ++t) step(std::integral_constant<bool, false>{}, t);
-  for (int t = t_mask; t < t_end; ++t) step(std::integral_constant<bool, true>{}, t);
+  constexpr std::integral_constant<bool, false> kFull{};
+  constexpr std::integral_constant<bool, true> kMasked{};
+  int t = t_begin;
+  for (; t + 1 < t_mask; t += 2) {
+    step(kFull, t, sA, sB);
+    step(kFull, t + 1, sB, sA);
+  }
+  if (t < t_mask) {
+    step(kFull, t, sA, sB);
+    ++t;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) sA[kb] = sB[kb];
+  }
+  for (; t + 1 < t_end; t += 2) {
+    step(kMasked, t, sA, sB);
+    step(kMasked, t + 1, sB, sA);
+  }
+  if (t < t_end) step(kMasked, t, sA, sB);
 
   // Epilogue: both lane halves hold parts of the row sum.
   const float l_tot = sum_xor32(l_run);
@@ -309,9 +395,9 @@ template <int D, typename TI, typename TO>
 static hipError_t launch3(const PrefillParams& p, bool causal, hipStream_t stream) {
   const int n = p.B * p.Hq * p.n_qtiles * p.n_splits;
   if (causal)
-    hipLaunchKernelGGL((prefill_kernel<D, TI, TO, true>), dim3(n), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, TI, TO, true>), dim3(n), dim3(64 * pf_waves(D)), 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, TI, TO, false>), dim3(n), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, TI, TO, false>), dim3(n), dim3(64 * pf_waves(D)), 0, stream, p);
   return hipGetLastError();
 }
 
