@@ -49,27 +49,42 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 // prefill planning
 // ---------------------------------------------------------------------------
 struct PrefillPlan {
+  int waves = 4;
   int n_qtiles = 0;
   int n_splits = 1;
   size_t ws_bytes = 0;
 };
 
+// Key splits for `base` workgroups of `waves` waves: two waves on every SIMD
+// (two 4-wave or one 8-wave workgroup per CU) is the target; a split keeps at
+// least 8 tiles (512 keys).
+int prefill_splits(int64_t base, int max_tiles, int waves) {
+  const int64_t target = (8 / waves) * (int64_t)planner_cus();
+  int S = 1;
+  while (base * S < target && S < 16 && max_tiles / (2 * S) >= 8) S *= 2;
+  return S;
+}
+
 PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split) {
   PrefillPlan pl;
-  pl.n_qtiles = ceil_div(Sq, pf_bm(D));
-  const int64_t base = (int64_t)B * Hq * pl.n_qtiles;
   const int max_tiles = ceil_div(Skv, PF_BN);
+  // Head size 128 uses 8-wave workgroups when they (with splits) still give
+  // every CU a workgroup; otherwise, and for head size 64, 4 waves.
+  int waves = 4;
+  if (D == 128) {
+    const int64_t base8 = (int64_t)B * Hq * ceil_div(Sq, 256);
+    const int S8 = allow_split ? prefill_splits(base8, max_tiles, 8) : 1;
+    if (base8 * S8 >= planner_cus()) waves = 8;
+  }
+  const int forced_w = env_int("FA_PREFILL_WAVES", 0);
+  if (D == 128 && (forced_w == 4 || forced_w == 8)) waves = forced_w;
+  pl.waves = waves;
+  pl.n_qtiles = ceil_div(Sq, 32 * waves);
+  const int64_t base = (int64_t)B * Hq * pl.n_qtiles;
   int S = 1;
   if (allow_split && base > 0) {
     const int forced = env_int("FA_PREFILL_SPLITS", 0);
-    if (forced > 0) {
-      S = std::min(forced, 64);
-    } else {
-      // Two waves on every SIMD: two 4-wave or one 8-wave workgroup per CU.
-      // Split the keys only while each split keeps at least 8 tiles (512 keys).
-      const int64_t target = (8 / pf_waves(D)) * (int64_t)planner_cus();
-      while (base * S < target && S < 16 && max_tiles / (2 * S) >= 8) S *= 2;
-    }
+    S = forced > 0 ? std::min(forced, 64) : prefill_splits(base, max_tiles, waves);
     S = std::max(1, std::min(S, std::max(1, max_tiles)));
   }
   pl.n_splits = S;
@@ -193,6 +208,7 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   p.Hkv = Hkv;
   p.Sq = Sq;
   p.Skv = Skv;
+  p.waves = pl.waves;
   p.n_qtiles = pl.n_qtiles;
   p.n_splits = pl.n_splits;
   p.q_neg = scale < 0.f;

@@ -6,36 +6,52 @@
 //
 // Split-reduction as in the dk-split of "perf(kernels): speed up
 // linear-attention prefill ~2.6x" (hip-ep, Summary), here over key ranges.
-// One wave per row; each lane owns 4 consecutive output columns.
+// A row is handled by D/4 lanes (4 consecutive output columns each), so a
+// 256-thread block covers 1024/D rows; the loads of four splits are issued
+// together.
 #include "fa_device.h"
 #include "fa_kernels.h"
 
 namespace fa {
 
-template <typename TO>
+template <typename TO, int TPR>
 __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
-  const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);
+  constexpr int RPB = 256 / TPR;
+  const int row = blockIdx.x * RPB + threadIdx.x / TPR;
+  const int d = 4 * (threadIdx.x % TPR);
   if (row >= p.rows) return;
   const int S = p.n_splits;
   const int64_t rows = p.rows;
+  const float* lse_p = p.part_lse + row;
+  const float* o_p = p.part_o + (int64_t)row * p.D + d;
+  const int64_t o_stride = rows * p.D;
   float mx = -INFINITY;
-  for (int s = 0; s < S; ++s) mx = fmaxf(mx, p.part_lse[s * rows + row]);
+  for (int s = 0; s < S; ++s) mx = fmaxf(mx, lse_p[s * rows]);
+  f32x4 acc = f32x4{};
   float sum = 0.f;
-  if (mx != -INFINITY)
-    for (int s = 0; s < S; ++s) sum += __expf(p.part_lse[s * rows + row] - mx);
-  const float inv = sum > 0.f ? 1.f / sum : 0.f;
-  for (int d = 4 * lane; d < p.D; d += 256) {
-    f32x4 acc = f32x4{};
-    if (mx != -INFINITY)
-      for (int s = 0; s < S; ++s) {
-        const float wgt = __expf(p.part_lse[s * rows + row] - mx) * inv;
-        if (wgt != 0.f) acc += wgt * *(const f32x4*)(p.part_o + (s * rows + row) * p.D + d);
+  if (mx != -INFINITY) {
+    for (int s0 = 0; s0 < S; s0 += 4) {
+      float l[4];
+      f32x4 o[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const bool ok = s0 + u < S;
+        l[u] = ok ? lse_p[(s0 + u) * rows] : -INFINITY;
+        o[u] = ok ? *(const f32x4*)(o_p + (s0 + u) * o_stride) : f32x4{};
       }
-    store4(TO{}, (char*)p.o + ((int64_t)row * p.D + d) * out_size<TO>::bytes, acc[0], acc[1],
-           acc[2], acc[3]);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float wgt = __expf(l[u] - mx);  // 0 for an empty split (lse -inf)
+        sum += wgt;
+        if (wgt != 0.f) acc += wgt * o[u];
+      }
+    }
   }
-  if (p.lse && lane == 0) {
+  const float inv = sum > 0.f ? 1.f / sum : 0.f;
+  acc *= inv;
+  store4(TO{}, (char*)p.o + ((int64_t)row * p.D + d) * out_size<TO>::bytes, acc[0], acc[1], acc[2],
+         acc[3]);
+  if (p.lse && d == 0) {
     const int h = row % p.Hq;
     const int i = (row / p.Hq) % p.Sq;
     const int b = row / (p.Hq * p.Sq);
@@ -43,19 +59,28 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
   }
 }
 
-hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream) {
-  const int blocks = (p.rows + 3) / 4;
-  switch (ot) {
-    case OutType::bf16:
-      hipLaunchKernelGGL(combine_kernel<out_bf16>, dim3(blocks), dim3(256), 0, stream, p);
-      break;
-    case OutType::f16:
-      hipLaunchKernelGGL(combine_kernel<out_f16>, dim3(blocks), dim3(256), 0, stream, p);
-      break;
-    default:
-      hipLaunchKernelGGL(combine_kernel<out_f32>, dim3(blocks), dim3(256), 0, stream, p);
+template <typename TO>
+hipError_t launch_combine_t(const CombineParams& p, hipStream_t stream) {
+  auto go = [&](auto kern, int tpr) {
+    const int rpb = 256 / tpr;
+    hipLaunchKernelGGL(kern, dim3((p.rows + rpb - 1) / rpb), dim3(256), 0, stream, p);
+  };
+  switch (p.D) {
+    case 64: go(combine_kernel<TO, 16>, 16); break;
+    case 128: go(combine_kernel<TO, 32>, 32); break;
+    case 256: go(combine_kernel<TO, 64>, 64); break;
+    case 512: go(combine_kernel<TO, 128>, 128); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
+}
+
+hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream) {
+  switch (ot) {
+    case OutType::bf16: return launch_combine_t<out_bf16>(p, stream);
+    case OutType::f16: return launch_combine_t<out_f16>(p, stream);
+    default: return launch_combine_t<out_f32>(p, stream);
+  }
 }
 
 }  // namespace fa

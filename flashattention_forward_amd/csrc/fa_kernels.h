@@ -20,7 +20,8 @@ struct PrefillParams {
   float* part_o;    // [S, B, Sq, Hq, D] fp32 when n_splits > 1
   float* part_lse;  // [S, B, Sq, Hq]
   int B, Hq, Hkv, Sq, Skv;
-  int n_qtiles;  // ceil(Sq / pf_bm(D))
+  int waves;     // waves per workgroup: 4 or 8 (8 only for head size 128)
+  int n_qtiles;  // ceil(Sq / (32 * waves))
   int n_splits;  // key splits per query tile
   int q_neg;     // 1: the scale was negative; the kernel uses -Q and |scale|
   float scale;       // |scale|, multiplies q.k
@@ -81,11 +82,10 @@ hipError_t launch_decode_mla(const DecodeMlaParams& p, InType it, hipStream_t st
 hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream);
 
 // Tile constants the host planner needs.
-// Prefill: waves per workgroup (each wave owns 32 query rows). Head size 128
-// runs one 8-wave workgroup per CU: every K/V tile copied into LDS then serves
-// 256 query rows, which halves the L2-to-CU traffic per flop.
-constexpr int pf_waves(int D) { return D == 128 ? 8 : 4; }
-constexpr int pf_bm(int D) { return 32 * pf_waves(D); }  // query rows per workgroup
+// Prefill: each wave owns 32 query rows; a workgroup has 4 or 8 waves (128 or
+// 256 query rows). With 8 waves (head size 128, one workgroup per CU) every
+// K/V tile copied into LDS serves 256 query rows, which halves the L2-to-CU
+// traffic per flop; 4 waves keep more workgroups for small problems.
 constexpr int PF_BM_MIN = 128;
 constexpr int PF_BN = 64;   // keys per prefill tile
 constexpr int DEC_TILE = 32;  // tokens per decode tile

@@ -43,19 +43,19 @@
 
 namespace fa {
 
-template <int D> struct PfCfg {
+template <int D, int NW_> struct PfCfg {
   static constexpr int NCH = D / 8;           // 16-byte chunks per key row
   static constexpr int NCB = NCH / 8;         // 8-chunk blocks per key row
   static constexpr int TILE = PF_BN * D * 2;  // bytes of one K (or V) tile
   static constexpr int LDS = 4 * TILE;        // 2 K stages + 2 V stages
-  static constexpr int NW = pf_waves(D);      // waves per workgroup
+  static constexpr int NW = NW_;              // waves per workgroup
   static constexpr int BM = 32 * NW;          // query rows per workgroup
   static constexpr int BPW = 8 * NCB / NW;    // 1 KB blocks of a tile each wave copies
 };
 
-template <int D, typename TI, typename TO, bool CAUSAL>
-__global__ __launch_bounds__(64 * pf_waves(D), 2) void prefill_kernel(PrefillParams p) {
-  using C = PfCfg<D>;
+template <int D, int NW, typename TI, typename TO, bool CAUSAL>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
+  using C = PfCfg<D, NW>;
   using T = in_traits<TI>;
   __shared__ __attribute__((aligned(16))) char smem[C::LDS];
 
@@ -391,14 +391,22 @@ __global__ __launch_bounds__(64 * pf_waves(D), 2) void prefill_kernel(PrefillPar
   }
 }
 
-template <int D, typename TI, typename TO>
-static hipError_t launch3(const PrefillParams& p, bool causal, hipStream_t stream) {
+template <int D, int NW, typename TI, typename TO>
+static hipError_t launch4(const PrefillParams& p, bool causal, hipStream_t stream) {
   const int n = p.B * p.Hq * p.n_qtiles * p.n_splits;
   if (causal)
-    hipLaunchKernelGGL((prefill_kernel<D, TI, TO, true>), dim3(n), dim3(64 * pf_waves(D)), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, NW, TI, TO, true>), dim3(n), dim3(64 * NW), 0, stream, p);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, TI, TO, false>), dim3(n), dim3(64 * pf_waves(D)), 0, stream, p);
+    hipLaunchKernelGGL((prefill_kernel<D, NW, TI, TO, false>), dim3(n), dim3(64 * NW), 0, stream, p);
   return hipGetLastError();
+}
+
+template <int D, typename TI, typename TO>
+static hipError_t launch3(const PrefillParams& p, bool causal, hipStream_t stream) {
+  if constexpr (D == 128) {
+    if (p.waves == 8) return launch4<D, 8, TI, TO>(p, causal, stream);
+  }
+  return launch4<D, 4, TI, TO>(p, causal, stream);
 }
 
 template <int D, typename TI>

@@ -96,6 +96,26 @@ def test_prefill_split_sweep(fa, splits, causal, monkeypatch):
     assert_lse(to_f64(lse), ref_lse, f"splits={splits}")
 
 
+WAVE_SHAPES = [s for s in SMALL if s[5] == 128] + [(1, 4, 2, 600, 2000, 128, True, "bf16", "bf16")]
+
+
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("splits", ["1", "4"])
+@pytest.mark.parametrize("shape", WAVE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_waves(fa, shape, waves, splits, monkeypatch):
+    """Head size 128 runs 4- or 8-wave workgroups (128 or 256 query rows); both
+    give the oracle's result, with and without key splits."""
+    B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
+    monkeypatch.setenv("FA_PREFILL_WAVES", waves)
+    monkeypatch.setenv("FA_PREFILL_SPLITS", splits)
+    log(f"prefill waves={waves} splits={splits} {shape}")
+    inp = fi.prefill_inputs(22, B, Hq, Hkv, Sq, Skv, D, causal, it, ot)
+    o, lse = run(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, it, f"waves={waves} splits={splits} {shape}")
+    assert_lse(to_f64(lse), ref_lse, f"waves={waves} splits={splits} {shape}")
+
+
 def test_prefill_no_keys(fa):
     import torch
     q = torch.randn(1, 40, 2, 64, device="cuda").to(torch.bfloat16)
