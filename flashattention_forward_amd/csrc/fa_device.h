@@ -191,6 +191,19 @@ __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_
 
 __device__ __forceinline__ u32x4 lds16(const char* p) { return *(const u32x4*)p; }
 
+// max / sum of a value over lanes l and l ^ 16 (v_permlane16_swap exchanges
+// the odd and even 16-lane rows of its two operands; no LDS).
+__device__ __forceinline__ float max_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float sum_xor16(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false,
+                                                  false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // max / sum of a value over lanes l and l ^ 32 (v_permlane32_swap, no LDS).
 __device__ __forceinline__ float max_xor32(float v) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false,
