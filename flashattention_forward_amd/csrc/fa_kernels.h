@@ -21,6 +21,7 @@ struct PrefillParams {
   float* part_lse;  // [S, B, Sq, Hq]
   int B, Hq, Hkv, Sq, Skv;
   int waves;     // waves per workgroup: 4 or 8 (8 only for head size 128)
+  int pingpong;  // 8 waves: the two-group ping-pong schedule (prefill_pp.hip)
   int n_qtiles;  // ceil(Sq / (32 * waves))
   int n_splits;  // key splits per query tile
   int q_neg;     // 1: the scale was negative; the kernel uses -Q and |scale|
@@ -78,6 +79,8 @@ struct CombineParams {
 hipError_t launch_prefill(const PrefillParams& p, int D, InType it, OutType ot, bool causal,
                           hipStream_t stream);
 hipError_t launch_decode_split(const DecodeSplitParams& p, InType it, hipStream_t stream);
+hipError_t launch_prefill_pp(const PrefillParams& p, InType it, OutType ot, bool causal,
+                             hipStream_t stream);
 hipError_t launch_decode_mla(const DecodeMlaParams& p, InType it, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream);
 

@@ -420,6 +420,7 @@ static hipError_t launch2(const PrefillParams& p, OutType ot, bool causal, hipSt
 
 hipError_t launch_prefill(const PrefillParams& p, int D, InType it, OutType ot, bool causal,
                           hipStream_t stream) {
+  if (D == 128 && p.waves == 8 && p.pingpong) return launch_prefill_pp(p, it, ot, causal, stream);
   if (D == 64)
     return it == InType::bf16 ? launch2<64, bf16_t>(p, ot, causal, stream)
                               : launch2<64, f16_t>(p, ot, causal, stream);

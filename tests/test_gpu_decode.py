@@ -58,7 +58,7 @@ def test_gqa_decode_small(fa, page_size, G):
     check(fa, inp, f"gqa page={page_size} G={G}")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 3, 8, 0])
+@pytest.mark.parametrize("splits", [1, 2, 3, 8, 24, 0])
 def test_gqa_decode_split_sweep(fa, splits):
     inp = fi.split_decode_inputs(40, 3, 8, 2, 128, [1500, 700, 64], 16)
     log(f"gqa decode splits={splits}")
@@ -122,7 +122,7 @@ def test_mla_decode_page_sizes(fa, page_size):
     check(fa, inp, f"mla page={page_size}")
 
 
-@pytest.mark.parametrize("splits", [1, 2, 4, 7, 0])
+@pytest.mark.parametrize("splits", [1, 2, 4, 7, 16, 0])
 def test_mla_decode_split_sweep(fa, splits):
     inp = _mla_ragged(52, 2, 64, 1024, 1, [1024, 999])
     log(f"mla splits={splits}")
