@@ -209,7 +209,7 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   p.Sq = Sq;
   p.Skv = Skv;
   p.waves = pl.waves;
-  p.pingpong = env_int("FA_PREFILL_PINGPONG", 1) != 0;
+  p.pingpong = env_int("FA_PREFILL_PINGPONG", 0) != 0;
   p.n_qtiles = pl.n_qtiles;
   p.n_splits = pl.n_splits;
   p.q_neg = scale < 0.f;

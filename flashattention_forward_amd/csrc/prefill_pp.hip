@@ -18,11 +18,14 @@
 // waves of one SIMD instead of inside one warpgroup). The wave in its matrix
 // phase raises its issue priority.
 //
-// Phase p = 2k holds A: M(k), B: V(k-1) + copies of K(k+2), V(k+1); phase
-// p = 2k + 1 holds A: V(k), B: M(k) + the wait for the copies of phase 2k-2.
-// K(j) lives in K stage j % 3 and V(j) in V stage j % 3: a stage is refilled
-// in the phase after both groups last read it, and a copy has three phases
-// to land. S needs one register set (V(k) consumes it before
+// Phase p = 2k holds A: M(k), B: V(k-1) + copies of K(k+1), V(k); phase
+// p = 2k + 1 holds A: V(k), B: M(k) + the wait for those copies. K(j) lives in
+// K stage j % 2 and V(j) in V stage j % 2: a stage is refilled in the phase
+// after both groups last read it.
+//
+// Measured on MI355X this schedule matches the single-group interleave of
+// prefill.hip (same time on the 512 x 16384 causal microbatch), so it is not
+// the default; FA_PREFILL_PINGPONG=1 selects it. S needs one register set (V(k) consumes it before
 // M(k+1) overwrites it) and P one (M(k+1) consumes it).
 #include "fa_device.h"
 #include "fa_kernels.h"
@@ -33,7 +36,7 @@ template <int D> struct PpCfg {
   static constexpr int NCH = D / 8;           // 16-byte chunks per key row
   static constexpr int NCB = NCH / 8;         // 8-chunk blocks per key row
   static constexpr int TILE = PF_BN * D * 2;  // bytes of one K (or V) tile
-  static constexpr int NST = 3;               // stages per ring
+  static constexpr int NST = 2;               // stages per ring
   static constexpr int LDS = 2 * NST * TILE;  // K ring + V ring
   static constexpr int BM = 256;              // 8 waves x 32 query rows
   static constexpr int BPW = 8 * NCB / 4;     // 1 KB blocks of a tile each group-B wave copies
@@ -267,36 +270,22 @@ __global__ __launch_bounds__(512, 2) void prefill_pp_kernel(PrefillParams p) {
       matrix(kOff, kOn, n);
       lds_barrier();
     } else {
-      // Copies run two tiles ahead: batch k = {K(k+2), V(k+1)} (those that
-      // exist) is issued in phase 2k and waited for at the end of phase 2k+3,
-      // where vmcnt leaves batch k+1 in flight. Batch -1 = {K(1), V(0)} goes
-      // out with K(0) before the first barrier.
-      auto wait_leaving = [&](int kk) {  // wait for all but batch kk
-        if (kk + 2 < n)
-          wait_vmcnt<2 * C::BPW>();
-        else if (kk + 1 < n)
-          wait_vmcnt<C::BPW>();
-        else
-          wait_vmcnt<0>();
-      };
       issue_k(0);
       wait_vmcnt<0>();
+      lds_barrier();
       if (1 < n) issue_k(1);
       issue_v(0);
       lds_barrier();
-      if (2 < n) issue_k(2);
-      if (1 < n) issue_v(1);
-      lds_barrier();
       matrix(kOn, kOff, 0);
-      wait_leaving(0);
+      wait_vmcnt<0>();
       lds_barrier();
       for (int k = 1; k < n; ++k) {
         vector(k - 1);
-        if (k + 2 < n) issue_k(k + 2);
-        if (k + 1 < n) issue_v(k + 1);
+        if (k + 1 < n) issue_k(k + 1);
+        issue_v(k);
         lds_barrier();
         matrix(kOn, kOn, k);
-        wait_leaving(k);
+        wait_vmcnt<0>();
         lds_barrier();
       }
       vector(n - 1);

@@ -116,6 +116,23 @@ def test_prefill_waves(fa, shape, waves, splits, monkeypatch):
     assert_lse(to_f64(lse), ref_lse, f"waves={waves} splits={splits} {shape}")
 
 
+@pytest.mark.parametrize("splits", ["1", "4"])
+@pytest.mark.parametrize("shape", WAVE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_pingpong(fa, shape, splits, monkeypatch):
+    """The two-group ping-pong schedule of the 8-wave kernel gives the oracle's
+    result too."""
+    B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
+    monkeypatch.setenv("FA_PREFILL_WAVES", "8")
+    monkeypatch.setenv("FA_PREFILL_PINGPONG", "1")
+    monkeypatch.setenv("FA_PREFILL_SPLITS", splits)
+    log(f"prefill ping-pong splits={splits} {shape}")
+    inp = fi.prefill_inputs(23, B, Hq, Hkv, Sq, Skv, D, causal, it, ot)
+    o, lse = run(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, it, f"ping-pong splits={splits} {shape}")
+    assert_lse(to_f64(lse), ref_lse, f"ping-pong splits={splits} {shape}")
+
+
 def test_prefill_no_keys(fa):
     import torch
     q = torch.randn(1, 40, 2, 64, device="cuda").to(torch.bfloat16)
