@@ -80,7 +80,7 @@ def traffic_for(kernel, sha):
         return None
     if not t or t.get("source_sha") != sha:
         return None
-    return t.get("bytes_per_launch")
+    return t.get("bytes_per_launch"), t.get("launch")
 
 
 def cpu_baseline(inp3, budget_s):
@@ -227,8 +227,8 @@ def main():
 
     sha_pf = source_sha("prefill.hip", "combine.hip", "fa_device.h")
     sha_dec = source_sha("decode_mla.hip", "combine.hip", "fa_device.h")
-    tr_pf = traffic_for("prefill", sha_pf)
-    tr_dec = traffic_for("decode_mla", sha_dec)
+    tr_pf, tr_pf_launch = traffic_for("prefill", sha_pf) or (None, None)
+    tr_dec, tr_dec_launch = traffic_for("decode_mla", sha_dec) or (None, None)
 
     result = {
         "metric": METRIC,
@@ -261,6 +261,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(pf_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": tr_pf,
+            "traffic_launch": tr_pf_launch,
             "kernel": "fa_prefill_ex call (prefill kernel + split combine), averaged over the "
                       "32 microbatch launches",
         },
@@ -275,6 +276,7 @@ def main():
                 "unit": "GB/s",
                 "frac": round(dec_gbs / PEAK_HBM_GBS, 4),
                 "traffic": tr_dec,
+                "traffic_launch": tr_dec_launch,
                 "kernel": "fa_decode_paged call (MLA decode kernel + split combine)",
             },
             "tflops": round(36507222016 * K / t_dec / 1e12, 1),

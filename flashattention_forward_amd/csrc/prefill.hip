@@ -6,12 +6,14 @@
 // score tile in registers and compress it to 16 bits before the second product,
 // size tiles to the chip's shared memory -- rebuilt for CDNA4 matrix cores:
 //
-//  * a workgroup is 4 waves; each wave owns 32 query rows of one head, so a
-//    workgroup covers 128 rows and shares every K/V tile of 64 keys in LDS;
+//  * each wave owns 32 query rows of one head; a workgroup of 4 or 8 waves
+//    (128 or 256 rows, chosen by the host) shares every K/V tile of 64 keys in
+//    LDS. With 8 waves a tile copied into LDS serves twice the rows, halving
+//    the L2-to-CU traffic per flop;
 //  * scores are computed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16 (A = K
 //    rows from LDS, B = the wave's Q rows held in registers for the whole pass).
 //    Each lane then owns one query column and 16 keys of each 32-key block, so
-//    the row max is in-lane plus one exchange with lane l ^ 32;
+//    the row max is in-lane plus one v_permlane32_swap;
 //  * the probabilities are rounded to 16 bits in registers and fed straight back
 //    as the B operand of O^T += V^T P^T. The contraction index of that product
 //    is relabelled to match the accumulator layout; the V^T operand comes from
@@ -23,14 +25,17 @@
 //    "perf: FlashAttention-3 style MLA PageAttention" (FlashInfer, change list
 //    item 3) adopts: the MFMAs of S(t+1) = K(t+1) Q^T are issued before the
 //    softmax of tile t, so the exp-heavy vector work of one tile overlaps the
-//    matrix-core work of the next;
+//    matrix-core work of the next. Each step is one straight-line block written
+//    out in issue order (K reads four MFMAs ahead, six vector ops of the
+//    softmax under each score MFMA, the transpose reads ahead of the PV MFMAs,
+//    the next tile's row max under them) and fenced with sched_barrier;
 //  * tiles are stored in 8 x 8 blocks of 16-byte chunks (blk_slot): a copy
 //    instruction moves 8 key rows x 128 contiguous bytes, and the K reads (16
 //    rows of one chunk) and the transposed V reads (4 rows x 4 chunks) each
 //    touch 64 distinct banks;
-//  * causal (bottom-right aligned) blocks stop at their last visible tile, waves
-//    skip tiles that none of their rows can see, and only tiles crossing the
-//    diagonal or the end of the keys are masked;
+//  * causal (bottom-right aligned) blocks stop at their last visible tile and
+//    only tiles crossing the diagonal or the end of the keys are masked (a tile
+//    above a wave's diagonal runs through the same block with probability 0);
 //  * the exponent uses exp2 with scale * log2(e) folded into one FMA, and the
 //    running max moves only when it grows by more than 2^8, so the O
 //    accumulators are rarely rescaled;
