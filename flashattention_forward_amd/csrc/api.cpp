@@ -99,6 +99,7 @@ struct DecodePlan {
   int n_splits = 1;
   int chunk = DEC_TILE;
   int n_hblk = 1;
+  int heads_per_wg = 64;  // MLA only
   size_t ws_bytes = 0;
 };
 
@@ -110,10 +111,18 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
   int64_t target;
   int min_splits = 1;
   if (layout == FA_KV_MLA_SHARED) {
-    pl.n_hblk = ceil_div(Hq, MLA_HEADS_PER_WG);
+    // 32 heads per workgroup when there are at most 32 (no idle head group);
+    // otherwise 64. (Two 32-head workgroups over one sequence's 64 heads read
+    // its rows once from HBM, the second copy coming from L2, but each CU then
+    // needs twice the bytes in flight for the same HBM rate: slower than
+    // splitting the keys.)
+    int nh = env_int("FA_MLA_HEADS", 0);
+    if (nh != 32 && nh != 64) nh = Hq <= 32 ? 32 : 64;
+    pl.heads_per_wg = nh;
+    pl.n_hblk = ceil_div(Hq, nh);
     units = (int64_t)B * pl.n_hblk;   // one workgroup per unit
-    target = planner_cus();           // one 4-wave workgroup per CU
-    min_splits = ceil_div(std::max(1, max_seq_len), MLA_MAX_CHUNK);
+    target = planner_cus();           // one 8-wave workgroup per CU
+    if (nh == 64) min_splits = ceil_div(std::max(1, max_seq_len), MLA_MAX_CHUNK);
   } else {
     pl.n_hblk = ceil_div(Hq / Hkv, 16);
     units = (int64_t)B * Hkv * pl.n_hblk;  // one wave per unit
@@ -331,6 +340,7 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     p.max_pages = max_pages_per_seq;
     p.num_pages = num_pages;
     p.max_seq_len = max_seq_len;
+    p.heads_per_wg = pl.heads_per_wg;
     p.n_hblk = pl.n_hblk;
     p.chunk = pl.chunk;
     p.n_splits = pl.n_splits;

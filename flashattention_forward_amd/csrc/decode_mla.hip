@@ -8,24 +8,35 @@
 // "Results" section measures batch x seq_len x 64 heads at page_size = 1, where
 // every token row is a separate gather. The same ideas, built for CDNA4:
 //
-//  * a workgroup (4 waves, 16 query heads each, one wave per SIMD) handles one
-//    sequence, 64 heads and one key split, so each 1152-byte row leaves HBM
-//    once and is read from LDS by both products;
-//  * rows are gathered through the page table into registers, two tiles of
-//    32 tokens ahead: every lane holds 9 x 16 bytes of each tile in flight,
-//    72 KB per CU. (Direct global-to-LDS copies keep far fewer bytes in
-//    flight per CU on this hardware and cap a random row gather at about half
-//    the HBM rate; plain vector loads do not.) When a tile's turn comes, its
-//    lanes write it into a 2-stage LDS ring; one barrier per tile publishes
-//    it and retires the stage two tiles back. The page table is resolved once
-//    per split into LDS, so no global load in the loop depends on another;
-//  * a tile is stored in 8 x 8 blocks of 16-byte chunks (blk_slot): wave w
-//    holds token rows 8w .. 8w + 7 and each store moves 8 rows x 128 bytes;
-//    the key reads (16 rows of 4 chunks, tokens in the order below) and the
-//    transposed value reads (ds_read_b64_tr_b16) are free of bank conflicts;
+//  * a workgroup (8 waves, two per SIMD) handles one sequence, NH = 64 or 32
+//    query heads and one key split; each 1152-byte row is read from HBM once
+//    per workgroup and from LDS by both products. Waves come in pairs over one
+//    group of 16 heads: each computes the partial scores over half of the 576
+//    dims, the pair adds its partials through LDS (so both hold the same
+//    scores, max and sum) and each accumulates half of the 512 output columns.
+//    No MFMA is repeated and a wave holds only half of the query fragments and
+//    of the O accumulators. With 64 heads the 4 pairs share every 32-token
+//    tile; with 32 heads a step covers 64 tokens, the 2 pairs of waves 0-3 take
+//    its first tile and those of waves 4-7 the second, and the two halves'
+//    states are merged at the end. The 32-head form lets two workgroups share
+//    a sequence's 64 heads without splitting its keys: they run side by side
+//    on one XCD, so the second read of each row is served by L2, and no
+//    partial results or combine pass are needed;
+//  * rows are gathered through the page table into registers a step or two
+//    ahead (72-80 KB in flight per CU). (Direct global-to-LDS copies keep far
+//    fewer bytes in flight per CU on this hardware and cap a random row gather
+//    at about half the HBM rate; plain vector loads do not.) When a step's turn
+//    comes its lanes write it into a 2-stage LDS ring; one barrier publishes it
+//    and retires the stage two steps back. Every lane loads the page-table
+//    entry of its own row two steps ahead of its use, so no global load waits
+//    on another inside the loop;
+//  * a tile is stored in 8 x 8 blocks of 16-byte chunks (blk_slot), each
+//    store moving 8 rows x 128 bytes; the key reads (16 rows of 4 chunks,
+//    tokens in the order below) and the transposed value reads
+//    (ds_read_b64_tr_b16) are free of bank conflicts;
 //  * S^T = K Q^T and O^T += V^T P^T on v_mfma_f32_16x16x32, the LDS reads
 //    issued several MFMAs ahead of their use; the running max moves only when
-//    it grows by more than 2^8, so the 128 O accumulators per lane are rarely
+//    it grows by more than 2^8, so the 64 O accumulators per lane are rarely
 //    rescaled; row reductions use lane swaps (no LDS);
 //  * tokens past the split's end are masked and rows without a valid token
 //    (or with a page id out of range) are zeroed in registers before they
@@ -38,26 +49,40 @@ namespace fa {
 constexpr int MLA_DQ = 576;
 constexpr int MLA_DV = 512;
 constexpr int MLA_ROWB = MLA_DQ * 2;            // 1152 bytes per row
-constexpr int MLA_NCH = MLA_DQ / 8;             // 72 chunks of 16 bytes
+constexpr int MLA_TILEB = DEC_TILE * MLA_ROWB;  // 36864 bytes per 32-token tile
 constexpr int MLA_NST = 2;                      // LDS ring stages
-constexpr int MLA_INFL = 2;                     // tiles in flight in registers
-constexpr int MLA_STAGE = DEC_TILE * MLA_ROWB;  // 36864 bytes
-constexpr int MLA_CPL = DEC_TILE * MLA_NCH / 256;  // 9 chunks per lane and tile
-constexpr int MLA_QW = (MLA_DQ / 32) * 1024;   // one wave's query fragments in LDS
+constexpr int MLA_THREADS = 512;                // 8 waves
+constexpr int MLA_QS = MLA_DQ / 32 / 2;         // query fragments per wave (half of the dims)
+constexpr int MLA_DVW = MLA_DV / 2;             // output columns per wave
 
-// LDS byte offset of chunk c of tile row r: block (r >> 3, c >> 3) of 9 per row band.
-__device__ __forceinline__ int mla_slot(int c, int r) {
-  return 16 * (64 * (9 * (r >> 3) + (c >> 3)) + blk_slot(r, c));
-}
+template <int NH> struct MlaCfg {
+  static constexpr int NHG = NH / 16;            // head groups (wave pairs per tile)
+  // With 64 heads a split's row ids are resolved into LDS once (so a split
+  // holds at most MLA_MAX_CHUNK tokens); with 32 heads the ring fills the LDS
+  // and every lane loads its row's page-table entry two steps ahead instead.
+  static constexpr bool ROWID_LDS = NH == 64;
+  static constexpr int TPS = 64 / NH;            // tiles per step
+  static constexpr int STEP_TOK = DEC_TILE * TPS;
+  static constexpr int INFL = NH == 64 ? 2 : 1;  // steps in flight in registers
+  // 16-byte chunks per lane and step: with 64 heads the two waves of a row band
+  // take blocks 0-4 and 4-8 of its 9 (both write block 4, with the same bytes);
+  // with 32 heads wave w stores row band w of the step's 8.
+  static constexpr int CPL = NH == 64 ? 5 : 9;
+  static constexpr int STAGE = TPS * MLA_TILEB;
+};
 
-template <typename TI, int PS>
-__global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
+template <typename TI, int PS, int NH>
+__global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaParams p) {
   using T = in_traits<TI>;
-  __shared__ __attribute__((aligned(16))) char smem[MLA_NST * MLA_STAGE];
-  __shared__ __attribute__((aligned(16))) char qsm[4 * MLA_QW];
-  __shared__ int rowid[MLA_MAX_CHUNK];
+  using C = MlaCfg<NH>;
+  constexpr int INFL = C::INFL, CPL = C::CPL;
+  __shared__ __attribute__((aligned(16))) char smem[MLA_NST * C::STAGE];
+  __shared__ __attribute__((aligned(16))) f32x4 xs[8][2][64];  // partial-score exchange
+  __shared__ int rowid[C::ROWID_LDS ? MLA_MAX_CHUNK : 1];        // pool row per token, -1: none
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  // Head group, half (of the dims and of O) and, with 32 heads, tile of the step.
+  const int hg = w % C::NHG, kh = (w / C::NHG) & 1, th = NH == 64 ? 0 : w >> 2;
   const int c16 = lane & 15, gq = lane >> 4;
 
   int blk = xcd_remap(blockIdx.x, gridDim.x);
@@ -66,88 +91,105 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
   blk /= S;
   const int hb = blk % p.n_hblk;
   const int b = blk / p.n_hblk;
-  const int head = hb * MLA_HEADS_PER_WG + 16 * w + c16;
+  const int head = hb * NH + 16 * hg + c16;
   const bool hvalid = head < p.Hq;
 
   const int seq_len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int t0 = split * p.chunk;
   const int n_tok = max(min(p.chunk, seq_len - t0), 0);
-  const int n_tiles = (n_tok + DEC_TILE - 1) / DEC_TILE;
+  const int n_steps = (n_tok + C::STEP_TOK - 1) / C::STEP_TOK;
 
-  // Resolve the split's page table into pool row ids (-1: page id out of
-  // range); all of a thread's page-table loads are issued before any is used.
-  {
-    const int32_t* ptab = p.page_table + (int64_t)b * p.max_pages;
-    constexpr int PER = MLA_MAX_CHUNK / 256;
+  // Staging: lane l of wave w holds chunk 8 cb + ((l >> 3) ^ (rb & 1)) of
+  // token row 8 rb + ((l & 7) ^ 4 ((l >> 4) & 1)) of a tile (the inverse of
+  // blk_slot), for its blocks cb; block cb of row band rb lives at byte
+  // 1024 (9 rb + cb) + 16 l of the tile.
+  const int rb = w & 3;
+  const int tile_row = 8 * rb + ((lane & 7) ^ (4 * ((lane >> 4) & 1)));
+  const int cp_tile = NH == 64 ? 0 : w >> 2;  // tile of the step this wave stores
+  const int cb0 = NH == 64 ? 4 * (w >> 2) : 0;
+  const int cp_row = DEC_TILE * cp_tile + tile_row;  // token within the step
+  const int cp_col = 16 * ((lane >> 3) ^ (rb & 1)) + 128 * cb0;
+  const int cp_dst = MLA_TILEB * cp_tile + 1024 * (9 * rb + cb0) + 16 * lane;
+
+  const int32_t* ptab = p.page_table + (int64_t)b * p.max_pages;
+  if constexpr (C::ROWID_LDS) {
+    // All of a thread's page-table loads are issued before any is used.
+    constexpr int PER = MLA_MAX_CHUNK / MLA_THREADS;
     int page[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = tid + 256 * k;
-      const int key = t0 + i;
-      const int pi = PS > 0 ? key / PS : key / p.page_size;
-      page[k] = i < n_tok ? ptab[pi] : -1;
+      const int key = t0 + tid + MLA_THREADS * k;
+      page[k] = tid + MLA_THREADS * k < n_tok ? ptab[PS > 0 ? key / PS : key / p.page_size] : -1;
     }
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int i = tid + 256 * k;
-      if (i < n_tok) {
-        const int key = t0 + i;
-        const int slot = PS > 0 ? key % PS : key % p.page_size;
-        rowid[i] = (unsigned)page[k] < (unsigned)p.num_pages ? page[k] * p.page_size + slot : -1;
-      }
+      const int key = t0 + tid + MLA_THREADS * k;
+      const int slot = PS > 0 ? key % PS : key % p.page_size;
+      rowid[tid + MLA_THREADS * k] =
+          (unsigned)page[k] < (unsigned)p.num_pages ? page[k] * p.page_size + slot : -1;
     }
+    __syncthreads();
   }
+  // Pool row (ROWID_LDS) or page-table entry of this lane's row in step s (a
+  // token past the split's end reads an entry that exists and is ignored).
+  auto pt_load = [&](int s) -> int {
+    const int tok = min(s * C::STEP_TOK + cp_row, max(n_tok - 1, 0));
+    if constexpr (C::ROWID_LDS) return rowid[tok];
+    const int key = t0 + tok;
+    return ptab[PS > 0 ? key / PS : key / p.page_size];
+  };
 
-  // Query fragments (B operand, 32 dims per MFMA step) live in LDS, each wave's
-  // own in lane order (fragment s of lane l at 1024 s + 16 l: conflict-free), so
-  // that the registers can hold the tiles in flight.
-  char* qw = qsm + MLA_QW * w;
+  // Query fragments (B operand, 32 dims per MFMA step) of this wave's half of
+  // the dims: steps 9 kh .. 9 kh + 8. A wave without valid heads uses head 0's
+  // (finite) query and stores nothing.
+  int pg[INFL];
+#pragma unroll
+  for (int d = 0; d < INFL; ++d) pg[d] = pt_load(d);
+  u32x4 qf[MLA_QS];
   {
     const char* qrow = (const char*)p.q + ((int64_t)b * p.Hq + (hvalid ? head : 0)) * MLA_ROWB;
-    u32x4 qv[MLA_DQ / 32];
 #pragma unroll
-    for (int s = 0; s < MLA_DQ / 32; ++s)
-      qv[s] = hvalid ? ldg16(qrow + (32 * s + 8 * gq) * 2) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < MLA_DQ / 32; ++s)
-      *(u32x4*)(qw + 1024 * s + 16 * lane) = p.q_neg ? neg16x8(qv[s]) : qv[s];
+    for (int i = 0; i < MLA_QS; ++i) qf[i] = ldg16(qrow + (32 * (MLA_QS * kh + i) + 8 * gq) * 2);
   }
-  __syncthreads();
 
   const char* pool = (const char*)p.pool;
-  // Lane l of wave w holds chunks 8i + ((l >> 3) ^ (w & 1)) (i < 9) of token row
-  // 8w + ((l & 7) ^ 4 * ((l >> 4) & 1)) of every tile: the inverse of blk_slot,
-  // so its chunk i goes to byte 1024 (9w + i) + 16 l of the stage.
-  const int cp_row = 8 * w + ((lane & 7) ^ (4 * ((lane >> 4) & 1)));
-  const int cp_col = 16 * ((lane >> 3) ^ (w & 1));
-  const int cp_dst = 1024 * MLA_CPL * w + 16 * lane;
-  u32x4 buf[MLA_INFL][MLA_CPL];
-  uint32_t badbits = 0;  // bit d: this lane's row of the tile in buf[d] is invalid
-  auto load = [&](int t, int d) {
-    const int tok = t * DEC_TILE + cp_row;
-    const int rid = tok < n_tok ? rowid[tok] : -1;
-    badbits = (badbits & ~(1u << d)) | ((rid < 0 ? 1u : 0u) << d);
-    const char* src = pool + (int64_t)max(rid, 0) * MLA_ROWB + cp_col;
+  u32x4 buf[INFL][CPL];
+  uint32_t badbits = 0;  // bit d: this lane's row in buf[d] is invalid
+  auto load = [&](int s, int d) {  // rows of step s, from pg[d]
+    const int tok = s * C::STEP_TOK + cp_row;
+    bool ok;
+    int64_t rid;
+    if constexpr (C::ROWID_LDS) {
+      ok = tok < n_tok && pg[d] >= 0;
+      rid = max(pg[d], 0);
+    } else {
+      const int key = t0 + tok;
+      const int slot = PS > 0 ? key % PS : key % p.page_size;
+      ok = tok < n_tok && (unsigned)pg[d] < (unsigned)p.num_pages;
+      rid = ok ? (int64_t)pg[d] * p.page_size + slot : 0;
+    }
+    badbits = (badbits & ~(1u << d)) | ((ok ? 0u : 1u) << d);
+    const char* src = pool + rid * MLA_ROWB + cp_col;
 #pragma unroll
-    for (int i = 0; i < MLA_CPL; ++i)
+    for (int i = 0; i < CPL; ++i)
       buf[d][i] = __builtin_nontemporal_load((const u32x4*)(src + 128 * i));
   };
-  auto store = [&](int t, int d) {
-    char* dst = smem + (t % MLA_NST) * MLA_STAGE + cp_dst;
+  auto store = [&](int s, int d) {
+    char* dst = smem + (s % MLA_NST) * C::STAGE + cp_dst;
     const bool bad = (badbits >> d) & 1;
     if (__ballot(bad)) {
 #pragma unroll
-      for (int i = 0; i < MLA_CPL; ++i)
+      for (int i = 0; i < CPL; ++i)
         *(u32x4*)(dst + 1024 * i) = bad ? u32x4{0, 0, 0, 0} : buf[d][i];
     } else {
 #pragma unroll
-      for (int i = 0; i < MLA_CPL; ++i) *(u32x4*)(dst + 1024 * i) = buf[d][i];
+      for (int i = 0; i < CPL; ++i) *(u32x4*)(dst + 1024 * i) = buf[d][i];
     }
   };
 
-  f32x4 oacc[MLA_DV / 16];
+  f32x4 oacc[MLA_DVW / 16];  // columns 256 kh + 16 db + 4 gq + i
 #pragma unroll
-  for (int db = 0; db < MLA_DV / 16; ++db) oacc[db] = f32x4{};
+  for (int db = 0; db < MLA_DVW / 16; ++db) oacc[db] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = p.scale_log2;
 
@@ -157,44 +199,39 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
   // {0, 3}, {1, 2}, {4, 7}, {5, 6}, and a pair must cover all 64 banks; with
   // this order the two groups of a pair read opposite bank halves. The score
   // S^T[kb][4 gq + i] of a lane is token 16 (gq >> 1) + 8 kb + 4 (gq & 1) + i.
-  // Key reads (mla_slot written out): row band 2 (c16 >> 3) + kb, chunk 4s + gq.
+  // Key reads: row band 2 (c16 >> 3) + kb, chunk 4s + gq of the tile.
   const int kp8 = c16 >> 3;
   const int kswz = 16 * ((c16 & 7) ^ (4 * (gq >> 1)));
-  const int koff0 = 18432 * kp8 + 128 * gq + kswz;
-  const int koff1 = 18432 * kp8 + 9216 + 128 * (gq ^ 1) + kswz;
+  const int koff0 = 18432 * kp8 + 128 * gq + kswz + 512 * MLA_QS * kh;
+  const int koff1 = 18432 * kp8 + 9216 + 128 * (gq ^ 1) + kswz + 512 * MLA_QS * kh;
   // Transposed value reads, lane j = c16: the PV contraction index 8 gq + k
   // is score row (k >> 2, 4 gq + (k & 3)), so the first read covers tokens
   // 16 (gq >> 1) + 4 (gq & 1) + j / 4 and the second the same + 8, in chunk
   // 2 db + e with e = (j & 3) >> 1, byte 8 (j & 1); the offset alternates with
   // the parity of db.
+  constexpr int NQK = 2 * MLA_QS, NPV = MLA_DVW / 16;
   const int e = (c16 & 3) >> 1;
-  const int tbase = 18432 * (gq >> 1) + 128 * e + 16 * (c16 >> 2) + 8 * (c16 & 1);
+  const int tbase = 18432 * (gq >> 1) + 128 * e + 16 * (c16 >> 2) + 8 * (c16 & 1) + 256 * NPV * kh;
   const int toffE = tbase + 64 * (gq & 1), toffO = tbase + 64 * ((gq & 1) ^ 1);
   const int tsecond = 9216 + 128 * (1 - 2 * e);
 
-  constexpr int NQK = 2 * (MLA_DQ / 32), NPV = MLA_DV / 16;
   constexpr int KPD = 6, VPD = 6;  // LDS reads issued this many MFMAs ahead
 
   // One tile: S^T = K Q^T, online softmax, O^T += V^T P^T. Every wave computes
-  // (a wave without valid heads works on zero queries and stores nothing): a
+  // (a wave without valid heads works on head 0's query and stores nothing): a
   // branch around the MFMAs would make the compiler shuttle the accumulators
   // between register files. Reads and MFMAs are written out in issue order and
   // fenced so that the order holds.
-  auto compute = [&](int t) {
-    const char* st = smem + (t % MLA_NST) * MLA_STAGE;
-    const int tok0 = t * DEC_TILE;
+  auto compute = [&](int s) {
+    const char* st = smem + (s % MLA_NST) * C::STAGE + MLA_TILEB * th;
+    const int tok0 = (s * C::TPS + th) * DEC_TILE;
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
     {
       const char* kp0 = st + koff0;
       const char* kp1 = st + koff1;
-      const char* qp = qw + 16 * lane;
-      u32x4 kf[NQK], qf[NQK / 2];
-      // MFMA i uses key fragment i and query fragment i / 2; read i brings
-      // key fragment i and, for even i, query fragment i / 2.
-      auto kread = [&](int i) {
-        kf[i] = lds16(((i & 1) ? kp1 : kp0) + 512 * (i >> 1));
-        if (!(i & 1)) qf[i >> 1] = lds16(qp + 1024 * (i >> 1));
-      };
+      u32x4 kf[NQK];
+      // MFMA i uses key fragment i (score block i & 1, step i >> 1 of this half).
+      auto kread = [&](int i) { kf[i] = lds16(((i & 1) ? kp1 : kp0) + 512 * (i >> 1)); };
 #pragma unroll
       for (int i = 0; i < KPD; ++i) kread(i);
 #pragma unroll
@@ -204,6 +241,16 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
         sacc[i & 1] = T::mma16(kf[i], qf[i >> 1], sacc[i & 1]);
       }
       __builtin_amdgcn_sched_barrier(0);
+    }
+    // Add the partner's partial scores (the other half of the dims).
+    xs[w][0][lane] = sacc[0];
+    xs[w][1][lane] = sacc[1];
+    lds_barrier();
+    sacc[0] += xs[w ^ C::NHG][0][lane];
+    sacc[1] += xs[w ^ C::NHG][1][lane];
+    if (p.q_neg) {  // a negative scale: the scores change sign
+      sacc[0] = -sacc[0];
+      sacc[1] = -sacc[1];
     }
     // The first value reads go out before the softmax (they do not depend on it).
     const char* vpE = st + toffE;
@@ -233,7 +280,7 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * sl2);
       l_run *= alpha;
 #pragma unroll
-      for (int db = 0; db < MLA_DV / 16; ++db) oacc[db] *= alpha;
+      for (int db = 0; db < NPV; ++db) oacc[db] *= alpha;
       m_run = m_new;
     }
     const float nb = m_run == -INFINITY ? 0.f : -m_run * sl2;
@@ -255,63 +302,98 @@ __global__ __launch_bounds__(256, 1) void decode_mla_kernel(DecodeMlaParams p) {
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Tile t sits in buf[t % 2]; it is waited for (vmcnt counts the 9 loads of
-  // the tile issued after it), stored, its registers reloaded with tile t + 2,
-  // published by the barrier and computed. The load schedule is the same on
-  // every path, so the compiler's own waits agree with it: loads are always
-  // issued (a tile past the split's end reads pool row 0 and is zeroed as
-  // invalid) and the loop runs an even number of steps (a padding tile is
-  // masked out entirely). The loop is unrolled by two so that every register
-  // index is static.
-  auto step = [&](int t, int d) {
-    wait_vmcnt<MLA_CPL>();
-    store(t, d);
-    load(t + MLA_INFL, d);
+  // Step s sits in buf[s % INFL]; it is waited for (vmcnt counts the loads of
+  // the INFL - 1 later steps: CPL rows and one page-table entry each), stored,
+  // its registers reloaded with step s + INFL (whose page entries arrived with
+  // it), the entries of step s + 2 INFL requested, the stage published by the
+  // barrier and computed. The load schedule is the same on every path, so the
+  // compiler's own waits agree with it: loads are always issued (rows past the
+  // split's end read pool row 0 and are zeroed as invalid) and the loop runs a
+  // multiple of INFL steps (a padding step is masked out entirely). The loop
+  // is unrolled by INFL so that every register index is static.
+  if constexpr (!C::ROWID_LDS)
+    wait_vmcnt<MLA_QS>();  // page entries of the first steps (the queries may still be in flight)
+#pragma unroll
+  for (int d = 0; d < INFL; ++d) {
+    load(d, d);
+    pg[d] = pt_load(d + INFL);
+  }
+  auto step = [&](int s, int d) {
+    wait_vmcnt<(CPL + !C::ROWID_LDS) * (INFL - 1)>();
+    store(s, d);
+    load(s + INFL, d);
+    pg[d] = pt_load(s + 2 * INFL);
     lds_barrier();
-    compute(t);
+    compute(s);
   };
-  load(0, 0);
-  load(1, 1);
-  for (int t = 0; t < n_tiles; t += MLA_INFL) {
-    step(t, 0);
-    step(t + 1, 1);
+  for (int s = 0; s < n_steps; s += INFL) {
+#pragma unroll
+    for (int d = 0; d < INFL; ++d) step(s + d, d);
   }
   wait_vmcnt<0>();
 
-  const float l_tot = sum_xor32(sum_xor16(l_run));
+  float l_tot = sum_xor32(sum_xor16(l_run));
+  if (NH == 32) {
+    // Merge the state of the step's second tile (waves 4-7) into that of the
+    // first (waves 0-3, same heads and columns) through LDS.
+    lds_barrier();  // every wave is done with the stages
+    char* xb = smem + (w & 3) * (16 * 1024 + 512);
+    if (th == 1) {
+#pragma unroll
+      for (int db = 0; db < NPV; ++db) *(f32x4*)(xb + 1024 * db + 16 * lane) = oacc[db];
+      ((float*)(xb + 16 * 1024))[lane] = m_run;
+      ((float*)(xb + 16 * 1024 + 256))[lane] = l_tot;
+    }
+    lds_barrier();
+    if (th == 1) return;
+    const float m1 = ((const float*)(xb + 16 * 1024))[lane];
+    const float l1 = ((const float*)(xb + 16 * 1024 + 256))[lane];
+    const float m = fmaxf(m_run, m1);
+    const float a0 = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m) * sl2);
+    const float a1 = m1 == -INFINITY ? 0.f : fast_exp2((m1 - m) * sl2);
+#pragma unroll
+    for (int db = 0; db < NPV; ++db)
+      oacc[db] = oacc[db] * a0 + *(const f32x4*)(xb + 1024 * db + 16 * lane) * a1;
+    l_tot = l_tot * a0 + l1 * a1;
+    m_run = m;
+  }
   if (!hvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
   const int64_t row = (int64_t)b * p.Hq + head;
   if (S == 1) {
-    char* orow = (char*)p.o + row * MLA_DV * 2;
+    char* orow = (char*)p.o + (row * MLA_DV + MLA_DVW * kh) * 2;
 #pragma unroll
-    for (int db = 0; db < MLA_DV / 16; ++db) {
+    for (int db = 0; db < NPV; ++db) {
       const u32x2 v{T::pack2(oacc[db][0] * inv, oacc[db][1] * inv),
                     T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
       *(u32x2*)(orow + (16 * db + 4 * gq) * 2) = v;
     }
-    if (p.lse && gq == 0) p.lse[row] = lse;
+    if (p.lse && gq == 0 && kh == 0) p.lse[row] = lse;
   } else {
     const int64_t rows = (int64_t)p.B * p.Hq;
-    float* orow = p.part_o + ((int64_t)split * rows + row) * MLA_DV;
+    float* orow = p.part_o + ((int64_t)split * rows + row) * MLA_DV + MLA_DVW * kh;
 #pragma unroll
-    for (int db = 0; db < MLA_DV / 16; ++db)
-      *(f32x4*)(orow + 16 * db + 4 * gq) = oacc[db] * inv;
-    if (gq == 0) p.part_lse[split * rows + row] = lse;
+    for (int db = 0; db < NPV; ++db) *(f32x4*)(orow + 16 * db + 4 * gq) = oacc[db] * inv;
+    if (gq == 0 && kh == 0) p.part_lse[split * rows + row] = lse;
   }
+}
+
+template <typename TI, int NH>
+static hipError_t mla_dispatch_nh(const DecodeMlaParams& p, hipStream_t stream) {
+  const int blocks = p.B * p.n_hblk * p.n_splits;
+  if (p.page_size == 1)
+    hipLaunchKernelGGL((decode_mla_kernel<TI, 1, NH>), dim3(blocks), dim3(MLA_THREADS), 0, stream, p);
+  else if (p.page_size == 16)
+    hipLaunchKernelGGL((decode_mla_kernel<TI, 16, NH>), dim3(blocks), dim3(MLA_THREADS), 0, stream, p);
+  else
+    hipLaunchKernelGGL((decode_mla_kernel<TI, 0, NH>), dim3(blocks), dim3(MLA_THREADS), 0, stream, p);
+  return hipGetLastError();
 }
 
 template <typename TI>
 static hipError_t mla_dispatch(const DecodeMlaParams& p, hipStream_t stream) {
-  const int blocks = p.B * p.n_hblk * p.n_splits;
-  if (p.page_size == 1)
-    hipLaunchKernelGGL((decode_mla_kernel<TI, 1>), dim3(blocks), dim3(256), 0, stream, p);
-  else if (p.page_size == 16)
-    hipLaunchKernelGGL((decode_mla_kernel<TI, 16>), dim3(blocks), dim3(256), 0, stream, p);
-  else
-    hipLaunchKernelGGL((decode_mla_kernel<TI, 0>), dim3(blocks), dim3(256), 0, stream, p);
-  return hipGetLastError();
+  return p.heads_per_wg == 32 ? mla_dispatch_nh<TI, 32>(p, stream) : mla_dispatch_nh<TI, 64>(p, stream);
 }
 
 hipError_t launch_decode_mla(const DecodeMlaParams& p, InType it, hipStream_t stream) {

@@ -59,8 +59,9 @@ struct DecodeMlaParams {
   float* part_o;  // [S, B, Hq, 512]
   float* part_lse;
   int B, Hq, page_size, max_pages, num_pages, max_seq_len;
-  int n_hblk;  // ceil(Hq / 64)
-  int chunk;   // tokens per split (multiple of 32, <= MLA_MAX_CHUNK)
+  int heads_per_wg;  // query heads per workgroup: 64 or 32
+  int n_hblk;        // ceil(Hq / heads_per_wg)
+  int chunk;         // tokens per split (multiple of 32; <= MLA_MAX_CHUNK with 64 heads)
   int n_splits;
   int q_neg;
   float scale, scale_log2;
@@ -91,8 +92,7 @@ hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream
 // traffic per flop; 4 waves keep more workgroups for small problems.
 constexpr int PF_BM_MIN = 128;
 constexpr int PF_BN = 64;   // keys per prefill tile
+constexpr int MLA_MAX_CHUNK = 2048;  // tokens per MLA split with 64 heads per workgroup
 constexpr int DEC_TILE = 32;  // tokens per decode tile
-constexpr int MLA_HEADS_PER_WG = 64;
-constexpr int MLA_MAX_CHUNK = 2048;  // tokens per MLA split (its row ids live in LDS)
 
 }  // namespace fa

@@ -121,9 +121,19 @@ def test_decode_validation(fa):
     call(B=0)  # empty batch: nothing enqueued
 
 
-def test_decode_split_planning(fa):
-    # MLA: 128 sequences of 2048 tokens, 64 heads -> 2 splits fill 256 CUs
-    assert fa.fa_decode_num_splits(128, 64, 1, 576, 512, 1, 2048, fa.FA_KV_MLA_SHARED) == 2
+def test_decode_split_planning(fa, monkeypatch):
+    mla = fa.FA_KV_MLA_SHARED
+    # MLA, 128 sequences of 2048 tokens, 64 heads per workgroup: 2 splits fill 256 CUs
+    assert fa.fa_decode_num_splits(128, 64, 1, 576, 512, 1, 2048, mla) == 2
+    assert (fa.fa_decode_workspace_size(128, 64, 1, 576, 512, 1, 2048, mla, 0)
+            == 2 * 128 * 64 * 513 * 4)
+    assert fa.fa_decode_num_splits(256, 64, 1, 576, 512, 1, 2048, mla) == 1
+    # 32 heads per workgroup: 128 sequences x 32 heads still split twice, 64 x 128 heads not
+    assert fa.fa_decode_num_splits(128, 32, 1, 576, 512, 1, 2048, mla) == 2
+    monkeypatch.setenv("FA_MLA_HEADS", "32")
+    assert fa.fa_decode_num_splits(64, 128, 1, 576, 512, 1, 2048, mla) == 1
+    assert fa.fa_decode_workspace_size(64, 128, 1, 576, 512, 1, 2048, mla, 0) == 0
+    monkeypatch.delenv("FA_MLA_HEADS")
     # GQA, 4 sequences x 8 K/V heads: many splits over 32768 tokens
     s = fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT)
     assert 16 <= s <= 128

@@ -129,6 +129,31 @@ def test_mla_decode_split_sweep(fa, splits):
     check(fa, inp, f"mla splits={splits}", num_splits=splits)
 
 
+@pytest.mark.parametrize("heads", ["32", "64"])
+@pytest.mark.parametrize("case", [(64, 1, 1, "bf16"), (48, 5, 3, "bf16"), (128, 16, 2, "fp16"),
+                                  (16, 1, 1, "bf16")])
+def test_mla_decode_heads_per_workgroup(fa, heads, case, monkeypatch):
+    """Both workgroup shapes (64 heads sharing each tile, or 32 heads taking the
+    two tiles of a 64-token step and merging at the end) on ragged lengths,
+    partial head blocks, page sizes 1 / 5 / 16 and split counts 1-3."""
+    Hq, page_size, splits, dtype = case
+    monkeypatch.setenv("FA_MLA_HEADS", heads)
+    inp = _mla_ragged(56, 3, Hq, 720, page_size, [720, 63, 97], dtype=dtype)
+    log(f"mla heads/wg={heads} Hq={Hq} page={page_size} splits={splits} {dtype}")
+    check(fa, inp, f"mla heads/wg={heads} Hq={Hq}", num_splits=splits)
+
+
+@pytest.mark.parametrize("heads", ["32", "64"])
+def test_mla_decode_long_single_split(fa, heads, monkeypatch):
+    """5000 tokens (157 tiles, ragged tail) with one split requested: 32 heads per
+    workgroup read the page table per step and take it in one split; 64 heads
+    hold a split's row ids in LDS, at most 2048 tokens, so the planner uses 3."""
+    monkeypatch.setenv("FA_MLA_HEADS", heads)
+    inp = _mla_ragged(57, 1, 64, 5000, 1, [5000])
+    log(f"mla long single split heads/wg={heads}")
+    check(fa, inp, f"mla long heads/wg={heads}", num_splits=1)
+
+
 def test_mla_decode_fp16_and_empty(fa):
     inp = _mla_ragged(53, 3, 64, 256, 1, [256, 0, 100], dtype="fp16")
     o, lse = check(fa, inp, "mla fp16")
@@ -163,3 +188,15 @@ def test_mla_decode_full_size_sampled(fa):
     assert_parity(o[batches], ref, "bf16", "workload 4 sampled")
     assert_lse(lse[batches], ref_lse, "workload 4 sampled")
     assert np.isfinite(o).all()
+
+
+def test_mla_decode_full_size_64_heads(fa, monkeypatch):
+    """Workload 4 with 64 heads per workgroup (two key splits and the combine)."""
+    monkeypatch.setenv("FA_MLA_HEADS", "64")
+    inp = fi.workload(4)
+    log("workload 4 full size, 64 heads per workgroup")
+    o, lse = run(fa, inp)
+    batches = [0, 5, 64, 127]
+    ref, ref_lse = oracle.decode_paged(inp, batches)
+    assert_parity(o[batches], ref, "bf16", "workload 4 sampled, 64 heads")
+    assert_lse(lse[batches], ref_lse, "workload 4 sampled, 64 heads")
