@@ -116,8 +116,11 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
     // its rows once from HBM, the second copy coming from L2, but each CU then
     // needs twice the bytes in flight for the same HBM rate: slower than
     // splitting the keys.)
+    // Without a workspace a sequence longer than one 64-head split holds takes
+    // 32-head workgroups, which need no split.
     int nh = env_int("FA_MLA_HEADS", 0);
-    if (nh != 32 && nh != 64) nh = Hq <= 32 ? 32 : 64;
+    if (nh != 32 && nh != 64)
+      nh = Hq <= 32 || (!allow_split && max_seq_len > MLA_MAX_CHUNK) ? 32 : 64;
     pl.heads_per_wg = nh;
     pl.n_hblk = ceil_div(Hq, nh);
     units = (int64_t)B * pl.n_hblk;   // one workgroup per unit
@@ -145,8 +148,10 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
   pl.chunk = ceil_div(tiles, S) * DEC_TILE;
   pl.n_splits = ceil_div(std::max(1, max_seq_len), pl.chunk);
   if (pl.n_splits < 1) pl.n_splits = 1;
+  // Partial outputs: fp32, or for MLA the 16-bit input type; fp32 lse.
+  const size_t part_elem = layout == FA_KV_MLA_SHARED ? 2 : sizeof(float);
   if (pl.n_splits > 1)
-    pl.ws_bytes = (size_t)pl.n_splits * B * Hq * (size_t)(D_v + 1) * sizeof(float);
+    pl.ws_bytes = (size_t)pl.n_splits * B * Hq * ((size_t)D_v * part_elem + sizeof(float));
   return pl;
 }
 
@@ -316,11 +321,13 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
   if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * Hq;
   if (rows > INT_MAX) return FA_ERR_SHAPE;
-  float* part_o = nullptr;
+  const bool part16 = layout == FA_KV_MLA_SHARED;
+  void* part_o = nullptr;
   float* part_lse = nullptr;
   if (pl.n_splits > 1) {
-    part_o = (float*)workspace;
-    part_lse = part_o + (size_t)pl.n_splits * rows * D_v;
+    part_o = workspace;
+    part_lse = (float*)((char*)workspace +
+                        (size_t)pl.n_splits * rows * D_v * (part16 ? 2 : sizeof(float)));
   }
   const InType it = dtype == FA_BF16 ? InType::bf16 : InType::f16;
   hipError_t e;
@@ -357,7 +364,7 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     p.seq_lens = seq_lens;
     p.o = o;
     p.lse = lse;
-    p.part_o = part_o;
+    p.part_o = (float*)part_o;
     p.part_lse = part_lse;
     p.B = B;
     p.Hq = Hq;
@@ -381,6 +388,7 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
   if (pl.n_splits > 1) {
     CombineParams c{};
     c.part_o = part_o;
+    c.part16 = part16;
     c.part_lse = part_lse;
     c.o = o;
     c.lse = lse;

@@ -56,8 +56,8 @@ struct DecodeMlaParams {
   const int32_t* seq_lens;
   void* o;  // [B, Hq, 512]
   float* lse;
-  float* part_o;  // [S, B, Hq, 512]
-  float* part_lse;
+  void* part_o;     // [S, B, Hq, 512] in the input's 16-bit type when n_splits > 1
+  float* part_lse;  // [S, B, Hq]
   int B, Hq, page_size, max_pages, num_pages, max_seq_len;
   int heads_per_wg;  // query heads per workgroup: 64 or 32
   int n_hblk;        // ceil(Hq / heads_per_wg)
@@ -70,7 +70,8 @@ struct DecodeMlaParams {
 // Split-KV log-sum-exp combine. Rows are in output order r = (b * Sq + i) * Hq + h;
 // part_o [S, rows, D], part_lse [S, rows]; o [rows, D]; lse index (b * Hq + h) * Sq + i.
 struct CombineParams {
-  const float* part_o;
+  const void* part_o;  // fp32, or the output's 16-bit type when part16
+  int part16;
   const float* part_lse;
   void* o;
   float* lse;

@@ -124,7 +124,9 @@ size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D,
  *   num_splits  0 = let the planner choose; n >= 1 asks for n key splits per
  *               sequence (clamped to what the shape allows)
  *   dtype       FA_BF16 or FA_FP16
- *   workspace   partial results of split-KV, or NULL (then num_splits is 1)
+ *   workspace   partial results of split-KV, or NULL (then num_splits is 1):
+ *               per split a normalised partial output (fp32 with FA_KV_SPLIT,
+ *               dtype with FA_KV_MLA_SHARED) and an fp32 log-sum-exp per row
  * Pool slots that no token of a sequence owns (tail slots, spare pages) are
  * never read as data, so they may hold anything, NaN included.
  */

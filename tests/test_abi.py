@@ -125,8 +125,9 @@ def test_decode_split_planning(fa, monkeypatch):
     mla = fa.FA_KV_MLA_SHARED
     # MLA, 128 sequences of 2048 tokens, 64 heads per workgroup: 2 splits fill 256 CUs
     assert fa.fa_decode_num_splits(128, 64, 1, 576, 512, 1, 2048, mla) == 2
+    # (16-bit partial outputs and fp32 lse per split)
     assert (fa.fa_decode_workspace_size(128, 64, 1, 576, 512, 1, 2048, mla, 0)
-            == 2 * 128 * 64 * 513 * 4)
+            == 2 * 128 * 64 * (512 * 2 + 4))
     assert fa.fa_decode_num_splits(256, 64, 1, 576, 512, 1, 2048, mla) == 1
     # 32 heads per workgroup: 128 sequences x 32 heads still split twice, 64 x 128 heads not
     assert fa.fa_decode_num_splits(128, 32, 1, 576, 512, 1, 2048, mla) == 2

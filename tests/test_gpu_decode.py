@@ -154,6 +154,24 @@ def test_mla_decode_long_single_split(fa, heads, monkeypatch):
     check(fa, inp, f"mla long heads/wg={heads}", num_splits=1)
 
 
+def test_mla_decode_long_without_workspace(fa):
+    """64 heads over 5000 tokens with no workspace: the planner takes 32-head
+    workgroups, which need no key split, instead of failing for want of one."""
+    import torch
+    inp = _mla_ragged(58, 2, 64, 5000, 1, [5000, 2500])
+    q, pool = to_dev(inp.q, "bf16"), to_dev(inp.pool, "bf16")
+    pt, sl = i32_dev(inp.page_table), i32_dev(inp.seq_lens)
+    o = torch.empty((inp.B, inp.Hq, 512), dtype=torch.bfloat16, device=q.device)
+    lse = torch.empty((inp.B, inp.Hq), dtype=torch.float32, device=q.device)
+    fa.fa_decode_paged(q, pool, pool.shape[0], pt, sl, o, lse, inp.B, inp.Hq, 1, 576, 512, 1,
+                       pt.shape[1], inp.max_seq_len, fa.FA_KV_MLA_SHARED, inp.scale, 0,
+                       fa.FA_BF16, None, 0, None)
+    torch.cuda.synchronize()
+    ref, ref_lse = oracle.decode_paged(inp)
+    assert_parity(to_f64(o), ref, "bf16", "mla long, no workspace")
+    assert_lse(to_f64(lse), ref_lse, "mla long, no workspace")
+
+
 def test_mla_decode_fp16_and_empty(fa):
     inp = _mla_ragged(53, 3, 64, 256, 1, [256, 0, 100], dtype="fp16")
     o, lse = check(fa, inp, "mla fp16")
