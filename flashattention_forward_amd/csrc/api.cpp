@@ -148,10 +148,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
   pl.chunk = ceil_div(tiles, S) * DEC_TILE;
   pl.n_splits = ceil_div(std::max(1, max_seq_len), pl.chunk);
   if (pl.n_splits < 1) pl.n_splits = 1;
-  // Partial outputs: fp32, or for MLA the 16-bit input type; fp32 lse.
-  const size_t part_elem = layout == FA_KV_MLA_SHARED ? 2 : sizeof(float);
+  // Partial outputs in the 16-bit input type, fp32 lse.
   if (pl.n_splits > 1)
-    pl.ws_bytes = (size_t)pl.n_splits * B * Hq * ((size_t)D_v * part_elem + sizeof(float));
+    pl.ws_bytes = (size_t)pl.n_splits * B * Hq * ((size_t)D_v * 2 + sizeof(float));
   return pl;
 }
 
@@ -233,8 +232,9 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   p.scale_log2 = std::max(p.scale * 1.4426950408889634f, 1e-30f);
   const int64_t rows = (int64_t)B * Sq * Hq;
   if (pl.n_splits > 1) {
-    p.part_o = (float*)workspace;
-    p.part_lse = p.part_o + (size_t)pl.n_splits * rows * D;
+    p.part_o = workspace;
+    p.part_lse = (float*)((char*)workspace +
+                          (size_t)pl.n_splits * rows * D * (out_dtype == FA_FP32 ? 4 : 2));
   }
   const InType it = in_dtype == FA_BF16 ? InType::bf16 : InType::f16;
   const OutType ot = out_dtype == FA_BF16 ? OutType::bf16
@@ -244,6 +244,7 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   if (pl.n_splits > 1) {
     CombineParams c{};
     c.part_o = p.part_o;
+    c.part16 = out_dtype != FA_FP32;
     c.part_lse = p.part_lse;
     c.o = o;
     c.lse = lse;
@@ -321,13 +322,11 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
   if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
   const int64_t rows = (int64_t)B * Hq;
   if (rows > INT_MAX) return FA_ERR_SHAPE;
-  const bool part16 = layout == FA_KV_MLA_SHARED;
   void* part_o = nullptr;
   float* part_lse = nullptr;
   if (pl.n_splits > 1) {
     part_o = workspace;
-    part_lse = (float*)((char*)workspace +
-                        (size_t)pl.n_splits * rows * D_v * (part16 ? 2 : sizeof(float)));
+    part_lse = (float*)((char*)workspace + (size_t)pl.n_splits * rows * D_v * 2);
   }
   const InType it = dtype == FA_BF16 ? InType::bf16 : InType::f16;
   hipError_t e;
@@ -364,7 +363,7 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     p.seq_lens = seq_lens;
     p.o = o;
     p.lse = lse;
-    p.part_o = (float*)part_o;
+    p.part_o = part_o;
     p.part_lse = part_lse;
     p.B = B;
     p.Hq = Hq;
@@ -388,7 +387,7 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
   if (pl.n_splits > 1) {
     CombineParams c{};
     c.part_o = part_o;
-    c.part16 = part16;
+    c.part16 = 1;
     c.part_lse = part_lse;
     c.o = o;
     c.lse = lse;

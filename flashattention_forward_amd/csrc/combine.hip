@@ -1,7 +1,7 @@
 // Split-KV combine: merges the partial results of S key ranges of one query row.
-// Each split s holds a normalised partial output O_s (fp32, or for paged MLA
-// decode the output's 16-bit type, which halves the partials' traffic) and
-// its log-sum-exp lse_s (fp32).
+// Each split s holds a normalised partial output O_s (in the output's type:
+// a 16-bit output halves the partials' traffic against fp32) and its
+// log-sum-exp lse_s (fp32).
 // With L = log sum_s exp(lse_s) the row's output is sum_s exp(lse_s - L) O_s and
 // its log-sum-exp is L (a split with lse_s = -inf contributes nothing; a row
 // whose splits are all empty gets O = 0, lse = -inf).

@@ -221,25 +221,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
   if (!hvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
+  // The output row, or with several splits this split's partial row (same
+  // 16-bit type; the combine weighs the partials by their lse).
   const int64_t row = (int64_t)b * p.Hq + hq;
-  if (S == 1) {
-    char* orow = (char*)p.o + row * D * 2;
+  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Hq + row;
+  char* orow = (char*)(S == 1 ? p.o : p.part_o) + prow * D * 2;
 #pragma unroll
-    for (int db = 0; db < D / 16; ++db) {
-      const int d = 16 * db + 4 * gq;
-      const u32x2 v{T::pack2(oacc[db][0] * inv, oacc[db][1] * inv),
-                    T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
-      *(u32x2*)(orow + d * 2) = v;
-    }
-    if (p.lse && gq == 0) p.lse[row] = lse;
-  } else {
-    const int64_t rows = (int64_t)p.B * p.Hq;
-    float* orow = p.part_o + ((int64_t)split * rows + row) * D;
-#pragma unroll
-    for (int db = 0; db < D / 16; ++db)
-      *(f32x4*)(orow + 16 * db + 4 * gq) = oacc[db] * inv;
-    if (gq == 0) p.part_lse[split * rows + row] = lse;
+  for (int db = 0; db < D / 16; ++db) {
+    const int d = 16 * db + 4 * gq;
+    const u32x2 v{T::pack2(oacc[db][0] * inv, oacc[db][1] * inv),
+                  T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
+    *(u32x2*)(orow + d * 2) = v;
   }
+  float* lrow = S == 1 ? p.lse : p.part_lse;
+  if (lrow && gq == 0) lrow[prow] = lse;
 }
 
 template <typename TI>

@@ -17,7 +17,7 @@ struct PrefillParams {
   const void* v;
   void* o;
   float* lse;       // [B, Hq, Sq] or null
-  float* part_o;    // [S, B, Sq, Hq, D] fp32 when n_splits > 1
+  void* part_o;     // [S, B, Sq, Hq, D] in the output type when n_splits > 1
   float* part_lse;  // [S, B, Sq, Hq]
   int B, Hq, Hkv, Sq, Skv;
   int waves;     // waves per workgroup: 4 or 8 (8 only for head size 128)
@@ -37,7 +37,7 @@ struct DecodeSplitParams {
   const int32_t* seq_lens;    // [B]
   void* o;                    // [B, Hq, D]
   float* lse;                 // [B, Hq] or null
-  float* part_o;              // [S, B, Hq, D]
+  void* part_o;               // [S, B, Hq, D] in the 16-bit input type
   float* part_lse;            // [S, B, Hq]
   int B, Hq, Hkv, page_size, max_pages, num_pages, max_seq_len;
   int n_hblk;    // ceil((Hq / Hkv) / 16) head blocks per K/V head

@@ -368,31 +368,26 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   if (!q_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
+  // The output row, or with several splits this split's partial row (in the
+  // output's type; the combine weighs the partials by their lse).
   const int64_t row = ((int64_t)b * p.Sq + qi) * p.Hq + hq;
-  if (S == 1) {
-    char* orow = (char*)p.o + row * D * out_size<TO>::bytes;
+  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Sq * p.Hq + row;
+  char* orow = (char*)(S == 1 ? p.o : p.part_o) + prow * D * out_size<TO>::bytes;
 #pragma unroll
-    for (int db = 0; db < D / 32; ++db)
+  for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * db + 8 * i4 + 4 * h;
-        store4(TO{}, orow + d * out_size<TO>::bytes, oacc[db][4 * i4] * inv,
-               oacc[db][4 * i4 + 1] * inv, oacc[db][4 * i4 + 2] * inv,
-               oacc[db][4 * i4 + 3] * inv);
-      }
-    if (p.lse && h == 0) p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
-  } else {
-    const int64_t rows = (int64_t)p.B * p.Sq * p.Hq;
-    float* orow = p.part_o + ((int64_t)split * rows + row) * D;
-#pragma unroll
-    for (int db = 0; db < D / 32; ++db)
-#pragma unroll
-      for (int i4 = 0; i4 < 4; ++i4) {
-        const int d = 32 * db + 8 * i4 + 4 * h;
-        store4(out_f32{}, orow + d, oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv,
-               oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
-      }
-    if (h == 0) p.part_lse[split * rows + row] = lse;
+    for (int i4 = 0; i4 < 4; ++i4) {
+      const int d = 32 * db + 8 * i4 + 4 * h;
+      store4(TO{}, orow + d * out_size<TO>::bytes, oacc[db][4 * i4] * inv,
+             oacc[db][4 * i4 + 1] * inv, oacc[db][4 * i4 + 2] * inv,
+             oacc[db][4 * i4 + 3] * inv);
+    }
+  if (h == 0) {
+    if (S == 1) {
+      if (p.lse) p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
+    } else {
+      p.part_lse[prow] = lse;
+    }
   }
 }
 

@@ -91,7 +91,8 @@ int fa_prefill(const void* q, const void* k, const void* v, void* o, int B, int 
  *             with a log-sum-exp combine kernel; workspace_bytes must then be at
  *             least fa_prefill_workspace_size(...) for the same shape, or the
  *             call fails with FA_ERR_WORKSPACE. The workspace holds no state
- *             between calls.
+ *             between calls. Per split it holds a normalised partial output
+ *             (in out_dtype) and an fp32 log-sum-exp per row.
  */
 int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
                   int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
@@ -125,8 +126,8 @@ size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D,
  *               sequence (clamped to what the shape allows)
  *   dtype       FA_BF16 or FA_FP16
  *   workspace   partial results of split-KV, or NULL (then num_splits is 1):
- *               per split a normalised partial output (fp32 with FA_KV_SPLIT,
- *               dtype with FA_KV_MLA_SHARED) and an fp32 log-sum-exp per row
+ *               per split a normalised partial output (in dtype) and an fp32
+ *               log-sum-exp per row
  * Pool slots that no token of a sequence owns (tail slots, spare pages) are
  * never read as data, so they may hold anything, NaN included.
  */

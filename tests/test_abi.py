@@ -116,7 +116,7 @@ def test_decode_validation(fa):
     assert _err(call, o=A + 2) == -4
     assert _err(call, pt=A + 1) == -4
     need = fa.fa_decode_workspace_size(2, 8, 2, 128, 128, 16, 4096, fa.FA_KV_SPLIT, 4)
-    assert need == 4 * 2 * 8 * 129 * 4
+    assert need == 4 * 2 * 8 * (128 * 2 + 4)  # 16-bit partials + fp32 lse per split
     assert _err(call, maxp=256, maxlen=4096, splits=4, ws=A, wsb=need - 16) == -5
     call(B=0)  # empty batch: nothing enqueued
 
