@@ -16,8 +16,12 @@ Workloads follow the shapes of the pages:
 
 Recipe (every tensor): ``numpy.random.default_rng([1000 + c, tensor_id])`` with
 ``c`` the workload number below and tensor ids q = 0, k = 1 (or the paged pool),
-v = 2, page permutation = 3, sequence lengths = 4; values are float32
-``standard_normal`` rounded once to bf16 / fp16 with round-to-nearest-even.
+v = 2, page permutation = 3, sequence lengths = 4, additive mask = 5; values are
+float32 ``standard_normal`` rounded once to bf16 / fp16 with round-to-nearest-even.
+
+Additive masks (``additive_mask``) take the shapes of the KQ mask that the
+llama.cpp page's opening paragraph counts as memory traffic: one [Sq, Skv]
+matrix (optionally one per batch entry), padded rows, -inf for hidden keys.
 """
 from __future__ import annotations
 
@@ -32,10 +36,11 @@ FP16 = "fp16"
 FP32 = "fp32"
 
 # Tensor ids of the seeding recipe.
-T_Q, T_K, T_V, T_POOL, T_PERM, T_LENS = 0, 1, 2, 1, 3, 4
+T_Q, T_K, T_V, T_POOL, T_PERM, T_LENS, T_MASK = 0, 1, 2, 1, 3, 4, 5
 
 # NaN bit patterns used to poison pool slots that no valid token owns.
 NAN_BITS = {BF16: 0x7FC0, FP16: 0x7E00}
+NEG_INF_BITS = {BF16: 0xFF80, FP16: 0xFC00}
 
 
 def rng_for(c: int, tensor_id: int) -> np.random.Generator:
@@ -88,6 +93,7 @@ class PrefillInputs:
     scale: float  # the float32 value handed to the kernel
     in_dtype: str
     out_dtype: str
+    mask: Optional[np.ndarray] = None  # uint16 bits [Bm, Sq, stride] (Bm 1 or B), or None
 
 
 @dataclasses.dataclass
@@ -127,6 +133,61 @@ def prefill_inputs(c: int, B: int, Hq: int, Hkv: int, Sq: int, Skv: int, D: int,
         scale = 1.0 / math.sqrt(D)
     return PrefillInputs(q, k, v, B, Hq, Hkv, Sq, Skv, D, bool(causal), f32(scale),
                          in_dtype, out_dtype or in_dtype)
+
+
+def additive_mask(c: int, Bm: int, Sq: int, Skv: int, kind: str, dtype: str = BF16,
+                  stride: Optional[int] = None) -> np.ndarray:
+    """uint16 bits [Bm, Sq, stride] of an additive mask (stride >= Skv; columns
+    >= Skv hold NaN, which no key may read). Query i sits at key position
+    p_i = Skv - Sq + i. Kinds:
+
+    * ``normal``: N(0,1) values with about one entry in eight -inf;
+    * ``packed``: several sequences packed into one microbatch at seeded cut
+      points of the key positions: key j is visible (0) to query i only inside
+      p_i's sequence and for j <= p_i, else -inf;
+    * ``bias``: a distance bias -2^-e (p_i - j) for j <= p_i and -inf beyond,
+      with a seeded e in 0..3 per batch entry;
+    * ``rows``: ``normal`` with every key of a few seeded rows -inf.
+    """
+    stride = Skv if stride is None else stride
+    assert stride >= Skv
+    rng = rng_for(c, T_MASK)
+    pos = (Skv - Sq + np.arange(Sq))[:, None]
+    key = np.arange(Skv)[None, :]
+    vals = np.empty((Bm, Sq, Skv), dtype=np.float32)
+    for b in range(Bm):
+        if kind in ("normal", "rows"):
+            x = rng.standard_normal(size=(Sq, Skv), dtype=np.float32)
+            x[rng.random(size=(Sq, Skv)) < 0.125] = -np.inf
+            if kind == "rows":
+                x[rng.choice(Sq, size=max(1, Sq // 16), replace=False)] = -np.inf
+        elif kind == "packed":
+            n_cut = int(rng.integers(1, 5))
+            cuts = np.sort(rng.choice(np.arange(1, max(Skv, 2)), size=min(n_cut, max(Skv - 1, 1)),
+                                      replace=False))
+            seq = np.searchsorted(cuts, np.arange(Skv), side="right")
+            same = seq[np.clip(pos[:, 0], 0, Skv - 1)][:, None] == seq[None, :]
+            x = np.where(same & (key <= pos), np.float32(0), np.float32(-np.inf))
+        elif kind == "bias":
+            slope = np.float32(2.0 ** -int(rng.integers(0, 4)))
+            x = np.where(key <= pos, -slope * (pos - key).astype(np.float32), np.float32(-np.inf))
+        else:
+            raise ValueError(kind)
+        vals[b] = x
+    bits = np.full((Bm, Sq, stride), NAN_BITS[dtype], dtype=np.uint16)
+    r = round_bits(vals, dtype)
+    r[np.isneginf(vals)] = NEG_INF_BITS[dtype]
+    bits[:, :, :Skv] = r
+    return bits
+
+
+def with_mask(inp: PrefillInputs, c: int, kind: str, batched: bool = False,
+              stride: Optional[int] = None) -> PrefillInputs:
+    """The same inputs with an additive mask attached (one per batch entry if
+    ``batched``)."""
+    inp.mask = additive_mask(c, inp.B if batched else 1, inp.Sq, inp.Skv, kind, inp.in_dtype,
+                             stride)
+    return inp
 
 
 def mla_decode_inputs(c: int, B: int, Hq: int, seq_len: int, D_qk: int = 576, D_v: int = 512,

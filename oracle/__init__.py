@@ -8,9 +8,11 @@ gathers paged K/V rows into contiguous arrays, and calls it.
 
 Definitions followed (the pages name the operation but print no formula):
 
-* attention: ``O = softmax(scale * Q K^T + mask) V`` with ``mask`` none or causal
-  aligned bottom-right, grouped-query head ``g = h // (Hq // Hkv)``; output 0 and
-  log-sum-exp -inf for a row with no visible key.
+* attention: ``O = softmax(scale * Q K^T + mask) V`` with ``mask`` causal aligned
+  bottom-right or none, plus optionally an explicit additive mask ``M[i][j]``
+  (finite or -inf) added to the scaled scores; grouped-query head
+  ``g = h // (Hq // Hkv)``; output 0 and log-sum-exp -inf for a row with no
+  visible key.
 * paged decode: token t of sequence b lives in physical page
   ``page_table[b][t // page_size]`` at slot ``t % page_size`` (the page-table
   gather of "perf: FlashAttention-3 style MLA PageAttention", section
@@ -55,7 +57,7 @@ def _load():
         P = ctypes.c_void_p
         I = ctypes.c_int64
         f.argtypes = [P, P, P, P, I, P, P, I, I, I, I, I, I, I, ctypes.c_int, ctypes.c_double,
-                      P, P, ctypes.c_int]
+                      P, I, I, P, P, ctypes.c_int]
         f.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -85,12 +87,14 @@ def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
 
 
-def attention_rows(q_rows, rb, rh, ri, k, v, Hq, Sq, causal, scale, nthreads=None):
+def attention_rows(q_rows, rb, rh, ri, k, v, Hq, Sq, causal, scale, nthreads=None, mask=None):
     """Attention for the listed query rows.
 
     q_rows [n, Dqk] float64; rb/rh/ri [n] batch, query-head and query index;
     k [B, Skv, Hkv, Dqk] and v [B, Skv, Hkv, Dv] float64. ``scale`` is used as a
-    double exactly as given. Returns (o_rows [n, Dv], lse_rows [n]).
+    double exactly as given. ``mask`` is None or a float64 additive mask
+    [Bm, Sq, stride] (Bm 1: shared by the batch; stride >= Skv; -inf hides a
+    key). Returns (o_rows [n, Dv], lse_rows [n]).
     """
     q_rows = np.ascontiguousarray(q_rows, dtype=np.float64)
     k = np.ascontiguousarray(k, dtype=np.float64)
@@ -104,23 +108,31 @@ def attention_rows(q_rows, rb, rh, ri, k, v, Hq, Sq, causal, scale, nthreads=Non
     assert v.shape[:3] == (B, Skv, Hkv) and q_rows.shape == (n, Dqk)
     o = np.zeros((n, Dv), dtype=np.float64)
     lse = np.zeros((n,), dtype=np.float64)
+    mptr, mb, ms = None, 0, 0
+    if mask is not None:
+        mask = np.ascontiguousarray(mask, dtype=np.float64)
+        assert mask.ndim == 3 and mask.shape[1] == Sq and mask.shape[2] >= Skv
+        assert mask.shape[0] in (1, B)
+        mptr, ms = _ptr(mask), mask.shape[2]
+        mb = 0 if mask.shape[0] == 1 else Sq * ms
     rc = _load().oracle_attention_rows(
         _ptr(q_rows), _ptr(rb), _ptr(rh), _ptr(ri), n, _ptr(k), _ptr(v), B, Hq, Hkv, Sq, Skv,
-        Dqk, Dv, int(bool(causal)), float(scale), _ptr(o), _ptr(lse),
+        Dqk, Dv, int(bool(causal)), float(scale), mptr, mb, ms, _ptr(o), _ptr(lse),
         int(nthreads or default_threads()))
     if rc != 0:
         raise RuntimeError(f"oracle_attention_rows failed ({rc})")
     return o, lse
 
 
-def attention(q, k, v, causal, scale, nthreads=None):
+def attention(q, k, v, causal, scale, nthreads=None, mask=None):
     """Full attention. q [B, Sq, Hq, Dqk], k [B, Skv, Hkv, Dqk], v [B, Skv, Hkv, Dv]
-    (float arrays). Returns (o [B, Sq, Hq, Dv], lse [B, Hq, Sq])."""
+    (float arrays), optional additive ``mask`` as in ``attention_rows``.
+    Returns (o [B, Sq, Hq, Dv], lse [B, Hq, Sq])."""
     q = np.asarray(q, dtype=np.float64)
     B, Sq, Hq, Dqk = q.shape
     bb, ii, hh = np.meshgrid(np.arange(B), np.arange(Sq), np.arange(Hq), indexing="ij")
     o, lse = attention_rows(q.reshape(-1, Dqk), bb.ravel(), hh.ravel(), ii.ravel(), k, v, Hq,
-                            Sq, causal, scale, nthreads)
+                            Sq, causal, scale, nthreads, mask)
     Dv = o.shape[1]
     return o.reshape(B, Sq, Hq, Dv), lse.reshape(B, Sq, Hq).transpose(0, 2, 1).copy()
 
@@ -133,13 +145,19 @@ def prefill_rows(inp, rows, nthreads=None):
     qb = inp.q[rows[:, 0], rows[:, 2], rows[:, 1], :]
     return attention_rows(widen(qb, inp.in_dtype), rows[:, 0], rows[:, 1], rows[:, 2],
                           widen(inp.k, inp.in_dtype), widen(inp.v, inp.in_dtype), inp.Hq, inp.Sq,
-                          inp.causal, float(inp.scale), nthreads)
+                          inp.causal, float(inp.scale), nthreads, _mask_of(inp))
+
+
+def _mask_of(inp):
+    m = getattr(inp, "mask", None)
+    return None if m is None else widen(m, inp.in_dtype)
 
 
 def prefill(inp, nthreads=None):
     """Full oracle output of a prefill input set: (o [B,Sq,Hq,D], lse [B,Hq,Sq])."""
     return attention(widen(inp.q, inp.in_dtype), widen(inp.k, inp.in_dtype),
-                     widen(inp.v, inp.in_dtype), inp.causal, float(inp.scale), nthreads)
+                     widen(inp.v, inp.in_dtype), inp.causal, float(inp.scale), nthreads,
+                     _mask_of(inp))
 
 
 def gather_paged(pool, page_table, seq_len, page_size, layout, b, Hkv, D_qk, D_v):

@@ -12,18 +12,22 @@
  * optimize tile kernel" (llama.cpp, opening paragraph: the FlashAttention
  * kernels and their KQ accumulators) and "perf: FlashAttention-3 style MLA
  * PageAttention" (FlashInfer, change list item 4: MLA uses one ckv matrix as
- * both K and V). The mask is either none or causal, aligned bottom-right (query
- * i of Sq sits at absolute position Skv - Sq + i); that is the reading under
- * which a 512-query microbatch attends to all prior keys, as in the llama.cpp
- * microbatch sweep ("Performance changes" table).
+ * both K and V). The mask is causal or not, aligned bottom-right (query i of Sq
+ * sits at absolute position Skv - Sq + i); that is the reading under which a
+ * 512-query microbatch attends to all prior keys, as in the llama.cpp
+ * microbatch sweep ("Performance changes" table). Optionally an explicit
+ * additive mask M[i][j] (finite or -infinity; the KQ mask that the llama.cpp
+ * page's opening paragraph counts as memory traffic) is added to the scaled
+ * scores, on top of the causal rule.
  *
  * Per query row (b, h, i):
  *   1. K/V head g = h / (Hq / Hkv)                  (grouped-query heads)
  *   2. visible keys J = { j : 0 <= j < Skv, and j <= i + Skv - Sq if causal }
- *   3. s_j = scale * sum_d q[d] * k_j[d]            (ascending d)
+ *   3. s_j = scale * sum_d q[d] * k_j[d] (+ M[i][j])   (ascending d)
  *   4. m = max_j s_j ; e_j = exp(s_j - m) ; l = sum_j e_j   (ascending j)
  *   5. o[d] = (sum_j e_j * v_j[d]) / l ; lse = m + log(l)   (natural log)
- *   6. no visible key: o = 0, lse = -infinity
+ *   6. no visible key (none in J, or M = -infinity on all of J): o = 0,
+ *      lse = -infinity
  *
  * Threads split the rows; each row is computed by one thread, start to end.
  */
@@ -42,6 +46,8 @@ typedef struct {
     int64_t B, Hq, Hkv, Sq, Skv, Dqk, Dv;
     int causal;
     double scale;
+    const double *mask;        /* additive mask, or NULL */
+    int64_t mask_bstride, mask_stride;  /* elements between batches / rows */
     double *o_rows;            /* [nrows, Dv] */
     double *lse_rows;          /* [nrows] */
     int64_t next;              /* next row to take (guarded by lock) */
@@ -70,10 +76,16 @@ static void one_row(oracle_job *J, int64_t r, double *s) {
         double acc = 0.0;
         for (int64_t d = 0; d < J->Dqk; ++d) acc += q[d] * kj[d];
         s[j] = J->scale * acc;
+        if (J->mask) s[j] += J->mask[b * J->mask_bstride + i * J->mask_stride + j];
     }
     double m = s[0];
     for (int64_t j = 1; j < nvis; ++j)
         if (s[j] > m) m = s[j];
+    if (m == -INFINITY) { /* every visible key masked out */
+        for (int64_t d = 0; d < J->Dv; ++d) o[d] = 0.0;
+        J->lse_rows[r] = -INFINITY;
+        return;
+    }
     double l = 0.0;
     for (int64_t j = 0; j < nvis; ++j) {
         s[j] = exp(s[j] - m);
@@ -114,17 +126,21 @@ static void *worker(void *arg) {
  *   q_rows  [nrows, Dqk]  the query vectors of the listed rows
  *   rb/rh/ri [nrows]      batch, query head and query index of each row
  *   k [B, Skv, Hkv, Dqk], v [B, Skv, Hkv, Dv]  (row-major, last index fastest)
+ *   mask  additive mask element (b, i, j) at mask[b * mask_bstride + i * mask_stride + j],
+ *         or NULL (mask_stride >= Skv; mask_bstride 0 shares one mask over the batch)
  *   o_rows [nrows, Dv], lse_rows [nrows]       outputs
  * Returns 0 on success, -1 on a bad argument, -2 when memory runs out.
  */
 int oracle_attention_rows(const double *q_rows, const int64_t *rb, const int64_t *rh,
                           const int64_t *ri, int64_t nrows, const double *k, const double *v,
                           int64_t B, int64_t Hq, int64_t Hkv, int64_t Sq, int64_t Skv,
-                          int64_t Dqk, int64_t Dv, int causal, double scale, double *o_rows,
-                          double *lse_rows, int nthreads) {
+                          int64_t Dqk, int64_t Dv, int causal, double scale,
+                          const double *mask, int64_t mask_bstride, int64_t mask_stride,
+                          double *o_rows, double *lse_rows, int nthreads) {
     if (nrows < 0 || B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || Sq < 0 || Skv < 0 ||
         Dqk <= 0 || Dv <= 0)
         return -1;
+    if (mask && (mask_stride < Skv || mask_bstride < 0)) return -1;
     for (int64_t r = 0; r < nrows; ++r)
         if (rb[r] < 0 || rb[r] >= B || rh[r] < 0 || rh[r] >= Hq || ri[r] < 0 || ri[r] >= Sq)
             return -1;
@@ -134,6 +150,7 @@ int oracle_attention_rows(const double *q_rows, const int64_t *rb, const int64_t
     J.k = k; J.v = v;
     J.B = B; J.Hq = Hq; J.Hkv = Hkv; J.Sq = Sq; J.Skv = Skv; J.Dqk = Dqk; J.Dv = Dv;
     J.causal = causal; J.scale = scale; J.o_rows = o_rows; J.lse_rows = lse_rows;
+    J.mask = mask; J.mask_bstride = mask_bstride; J.mask_stride = mask_stride;
     pthread_mutex_init(&J.lock, NULL);
     if (nthreads < 1) nthreads = 1;
     if (nthreads > 256) nthreads = 256;

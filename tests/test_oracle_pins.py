@@ -4,12 +4,16 @@ Kinds of pin used (the pages print no worked attention example, so none is a
 printed value):
 
 * library routines: torch's float64 ``scaled_dot_product_attention`` on the CPU,
-  with its own grouped-query expansion and its own bottom-right causal bias;
+  with its own grouped-query expansion and its own bottom-right causal bias, and
+  with a float ``attn_mask`` for the explicit additive mask;
   numpy's ``logaddexp`` for the log-sum-exp split identity;
 * closed forms: scale 0 gives the mean of the visible V rows and lse = ln(n);
   one query and two keys give the logistic weights;
 * invariants: constant V rows, a one-hot dominant score, key permutation,
-  causal first query, microbatch concatenation, paging and MLA sharing.
+  causal first query, microbatch concatenation, paging and MLA sharing; for the
+  additive mask: a zero mask and a 0/-inf causal matrix reproduce the unmasked
+  and causal results bit for bit, a row-constant mask shifts only lse, single
+  visible keys and fully hidden rows, and per-batch masks.
 
 A wrong sign, a dropped scale, a transposed operand, a wrong head group or an
 off-by-one causal offset each fails at least one of these.
@@ -197,6 +201,121 @@ def test_thread_count_does_not_change_result(oracle_lib):
     o7, l7 = oracle.attention(q, k, v, True, 0.3, nthreads=7)
     np.testing.assert_array_equal(o1, o7)
     np.testing.assert_array_equal(l1, l7)
+
+
+# --------------------------------------------------------------------------
+# explicit additive mask
+# --------------------------------------------------------------------------
+
+def _sdpa_masked(q, k, v, mask, causal, scale):
+    """torch float64 SDPA with a float attn_mask [Bm, Sq, Skv] (broadcast over
+    heads); the causal rule is folded in as -inf above the bottom-right
+    diagonal, built here from key and query positions."""
+    tq = torch.from_numpy(q).permute(0, 2, 1, 3)
+    tk = torch.from_numpy(k).permute(0, 2, 1, 3)
+    tv = torch.from_numpy(v).permute(0, 2, 1, 3)
+    Sq, Skv = q.shape[1], k.shape[1]
+    m = torch.from_numpy(mask.copy())
+    if causal:
+        hide = torch.arange(Skv)[None, :] > torch.arange(Sq)[:, None] + (Skv - Sq)
+        m = m.masked_fill(hide[None], float("-inf"))
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m[:, None], scale=scale,
+                                       enable_gqa=q.shape[2] != k.shape[2])
+    return o.permute(0, 2, 1, 3).numpy()
+
+
+@pytest.mark.parametrize("trial", range(24))
+def test_mask_matches_torch_sdpa(oracle_lib, trial):
+    """Random finite masks with scattered -inf (never a whole visible row),
+    shared by the batch or one per batch entry, with and without the causal
+    rule: against torch's float64 SDPA with a float attn_mask."""
+    r = np.random.default_rng(100 + trial)
+    B, Hkv, G = int(r.integers(1, 3)), int(r.integers(1, 3)), int(r.integers(1, 4))
+    Hq = Hkv * G
+    Skv = int(r.integers(2, 12))
+    causal = bool(trial % 2)
+    Sq = int(r.integers(1, Skv + 1)) if causal else int(r.integers(1, 12))
+    D = int(r.integers(1, 9))
+    scale = float(r.uniform(0.1, 1.5))
+    q, k, v = r.standard_normal((B, Sq, Hq, D)), r.standard_normal((B, Skv, Hkv, D)), \
+        r.standard_normal((B, Skv, Hkv, D))
+    Bm = B if trial % 3 == 0 else 1
+    mask = 2.0 * r.standard_normal((Bm, Sq, Skv))
+    hide = r.random((Bm, Sq, Skv)) < 0.3
+    hide[..., 0] = False  # key 0 is visible to every row (also under the causal rule)
+    mask[hide] = -np.inf
+    o, lse = oracle.attention(q, k, v, causal, scale, mask=mask)
+    ref = _sdpa_masked(q, k, v, np.broadcast_to(mask, (B, Sq, Skv)), causal, scale)
+    np.testing.assert_allclose(o, ref, rtol=1e-12, atol=1e-12)
+    assert np.all(np.isfinite(lse))
+
+
+def test_zero_mask_is_no_mask(oracle_lib):
+    """An all-zero mask changes nothing, bit for bit."""
+    q, k, v = _rand(2, 5, 4, 6), _rand(2, 9, 2, 6), _rand(2, 9, 2, 6)
+    for causal in (False, True):
+        o0, l0 = oracle.attention(q, k, v, causal, 0.4)
+        o1, l1 = oracle.attention(q, k, v, causal, 0.4, mask=np.zeros((1, 5, 9)))
+        assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_causal_mask_matrix_equals_causal_rule(oracle_lib):
+    """A 0 / -inf matrix of the bottom-right causal pattern, without the causal
+    flag, gives exactly the causal result (with a padded row stride)."""
+    Sq, Skv = 6, 10
+    q, k, v = _rand(1, Sq, 2, 5), _rand(1, Skv, 1, 5), _rand(1, Skv, 1, 5)
+    mask = np.full((1, Sq, Skv + 3), np.nan)
+    for i in range(Sq):
+        for j in range(Skv):
+            mask[0, i, j] = 0.0 if j <= i + Skv - Sq else -np.inf
+    o0, l0 = oracle.attention(q, k, v, True, 0.9)
+    o1, l1 = oracle.attention(q, k, v, False, 0.9, mask=mask)
+    assert np.array_equal(o0, o1) and np.array_equal(l0, l1)
+
+
+def test_row_constant_mask_shifts_lse_only(oracle_lib):
+    """Adding c_i to every key of row i leaves o unchanged and adds c_i to lse."""
+    Sq, Skv = 4, 7
+    q, k, v = _rand(1, Sq, 3, 4), _rand(1, Skv, 3, 4), _rand(1, Skv, 3, 4)
+    c = np.array([0.5, -3.0, 7.25, 0.0])
+    mask = np.repeat(c[:, None], Skv, axis=1)[None]
+    o0, l0 = oracle.attention(q, k, v, False, 0.6)
+    o1, l1 = oracle.attention(q, k, v, False, 0.6, mask=mask)
+    np.testing.assert_allclose(o1, o0, rtol=0, atol=1e-13)
+    np.testing.assert_allclose(l1, l0 + c[None, None, :], rtol=0, atol=1e-12)
+
+
+def test_single_visible_key_and_empty_rows(oracle_lib):
+    """Row 0 sees only key 3 (o = v_3, lse = score_3 + mask_3); row 1 sees
+    nothing (o = 0, lse = -inf); row 2 sees only key 4 (o = v_4). With the
+    causal rule on top (Sq = 3 < Skv = 5: row 0 sits at position 2), row 0
+    loses key 3 and becomes empty while row 2 keeps key 4."""
+    Sq, Skv, D = 3, 5, 4
+    q, k, v = _rand(1, Sq, 1, D), _rand(1, Skv, 1, D), _rand(1, Skv, 1, D)
+    mask = np.full((1, Sq, Skv), -np.inf)
+    mask[0, 0, 3] = 1.5
+    mask[0, 2, 4] = 0.0
+    o, lse = oracle.attention(q, k, v, False, 0.8, mask=mask)
+    np.testing.assert_array_equal(o[0, 0, 0], v[0, 3, 0])
+    assert lse[0, 0, 0] == pytest.approx(0.8 * float(q[0, 0, 0] @ k[0, 3, 0]) + 1.5, abs=1e-13)
+    assert np.all(o[0, 1, 0] == 0) and lse[0, 0, 1] == -np.inf
+    np.testing.assert_array_equal(o[0, 2, 0], v[0, 4, 0])
+    o2, lse2 = oracle.attention(q, k, v, True, 0.8, mask=mask)
+    assert np.all(o2[0, 0, 0] == 0) and lse2[0, 0, 0] == -np.inf
+    np.testing.assert_array_equal(o2[0, 2, 0], v[0, 4, 0])
+
+
+def test_batched_mask_equals_per_batch_calls(oracle_lib):
+    """One mask per batch entry equals separate single-batch calls."""
+    q, k, v = _rand(3, 4, 2, 5), _rand(3, 6, 2, 5), _rand(3, 6, 2, 5)
+    mask = _rand(3, 4, 6)
+    mask[_rand(3, 4, 6) > 1.0] = -np.inf
+    mask[..., 0] = 0.0
+    o, lse = oracle.attention(q, k, v, False, 0.5, mask=mask)
+    for b in range(3):
+        ob, lb = oracle.attention(q[b:b + 1], k[b:b + 1], v[b:b + 1], False, 0.5,
+                                  mask=mask[b:b + 1])
+        assert np.array_equal(o[b:b + 1], ob) and np.array_equal(lse[b:b + 1], lb)
 
 
 def test_bad_arguments_raise(oracle_lib):
