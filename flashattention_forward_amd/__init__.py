@@ -1,14 +1,15 @@
 """Fused attention forward for AMD MI355X (gfx950): Python binding of libfa.so.
 
 The functions named like the C entry points (``fa_prefill``, ``fa_prefill_ex``,
-``fa_decode_paged``, the workspace-size queries, ``fa_strerror``) marshal their
+``fa_prefill_mask``, ``fa_decode_paged``, the workspace-size queries, ``fa_strerror``) marshal their
 arguments and call the library; every step of the computation runs in the HIP
 kernels. torch is used only for device memory and streams. ``prefill`` and
 ``decode_paged`` are conveniences that allocate outputs and workspace with torch
 and then call the same entry points.
 
 There is no fallback: if ``libfa.so`` has not been built, importing this package
-raises ImportError (build it with ``python -m flashattention_forward_amd.build``).
+raises ImportError (build it with ``python flashattention_forward_amd/build.py``),
+and so does a library older than this binding (a missing entry point).
 """
 from __future__ import annotations
 
@@ -19,7 +20,8 @@ from typing import Optional
 
 __all__ = [
     "FA_BF16", "FA_FP16", "FA_FP32", "FA_KV_SPLIT", "FA_KV_MLA_SHARED", "FaError",
-    "fa_prefill", "fa_prefill_ex", "fa_prefill_workspace_size", "fa_decode_paged",
+    "fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_prefill_workspace_size",
+    "fa_decode_paged",
     "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "fa_version",
     "prefill", "decode_paged", "LIB_PATH",
 ]
@@ -29,10 +31,16 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfa.so")
 FA_BF16, FA_FP16, FA_FP32 = 0, 1, 2
 FA_KV_SPLIT, FA_KV_MLA_SHARED = 0, 1
 
+_BUILD_HINT = "run `python flashattention_forward_amd/build.py`"
 if not os.path.exists(LIB_PATH):
-    raise ImportError(f"{LIB_PATH} is not built; run `python -m flashattention_forward_amd.build`")
+    raise ImportError(f"{LIB_PATH} is not built; {_BUILD_HINT}")
 
 _lib = ctypes.CDLL(LIB_PATH)
+for _name in ("fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_prefill_workspace_size",
+              "fa_decode_paged", "fa_decode_workspace_size", "fa_decode_num_splits",
+              "fa_strerror", "fa_version"):
+    if not hasattr(_lib, _name):
+        raise ImportError(f"{LIB_PATH} lacks {_name} (older than its sources); {_BUILD_HINT}")
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
@@ -43,6 +51,10 @@ _lib.fa_prefill.restype = _I
 _lib.fa_prefill_ex.argtypes = [_P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _I, _P,
                                _Z, _P]
 _lib.fa_prefill_ex.restype = _I
+_L = ctypes.c_int64
+_lib.fa_prefill_mask.argtypes = [_P, _P, _P, _P, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
+                                 _I, _I, _P, _Z, _P]
+_lib.fa_prefill_mask.restype = _I
 _lib.fa_prefill_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I]
 _lib.fa_prefill_workspace_size.restype = _Z
 _lib.fa_decode_paged.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
@@ -114,6 +126,18 @@ def fa_prefill_ex(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, in_dty
                               _stream(stream)), "fa_prefill_ex")
 
 
+def fa_prefill_mask(q, k, v, mask, mask_stride, mask_batch_stride, o, lse, B, Hq, Hkv, Sq, Skv,
+                    D, causal, scale, in_dtype, out_dtype, workspace=None, workspace_bytes=0,
+                    stream=None) -> None:
+    if workspace is not None and not isinstance(workspace, int) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.fa_prefill_mask(_ptr(q), _ptr(k), _ptr(v), _ptr(mask), int(mask_stride),
+                                int(mask_batch_stride), _ptr(o), _ptr(lse), B, Hq, Hkv, Sq, Skv,
+                                D, int(bool(causal)), float(scale), int(in_dtype),
+                                int(out_dtype), _ptr(workspace), int(workspace_bytes),
+                                _stream(stream)), "fa_prefill_mask")
+
+
 def fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal) -> int:
     return int(_lib.fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, int(bool(causal))))
 
@@ -163,10 +187,12 @@ def _workspace(nbytes: int, device):
 
 
 def prefill(q, k, v, *, causal: bool, scale: Optional[float] = None, out=None, out_dtype=None,
-            return_lse: bool = False, allow_split: bool = True, stream=None):
+            return_lse: bool = False, allow_split: bool = True, mask=None, stream=None):
     """Attention prefill on torch tensors q [B, Sq, Hq, D], k/v [B, Skv, Hkv, D]
-    (bf16 or fp16, contiguous, on the GPU). Returns o [B, Sq, Hq, D] (and lse
-    [B, Hq, Sq] fp32 if asked)."""
+    (bf16 or fp16, contiguous, on the GPU). ``mask`` is None or an additive mask
+    of q's dtype, [Sq, W] or [B, Sq, W] with W >= Skv rounded up to 4 and a
+    multiple of 4 (contiguous). Returns o [B, Sq, Hq, D] (and lse [B, Hq, Sq]
+    fp32 if asked)."""
     import torch
     B, Sq, Hq, D = q.shape
     _, Skv, Hkv, _ = k.shape
@@ -181,8 +207,18 @@ def prefill(q, k, v, *, causal: bool, scale: Optional[float] = None, out=None, o
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
     ws = _workspace(fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal), q.device) \
         if allow_split else None
-    fa_prefill_ex(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale, _fa_dtype(q.dtype),
-                  _fa_dtype(out.dtype), ws, 0 if ws is None else ws.numel() * 4, stream)
+    wsb = 0 if ws is None else ws.numel() * 4
+    if mask is None:
+        fa_prefill_ex(q, k, v, out, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+                      _fa_dtype(q.dtype), _fa_dtype(out.dtype), ws, wsb, stream)
+    else:
+        if mask.dtype != q.dtype or not mask.is_contiguous() or mask.shape[-2] != Sq:
+            raise ValueError("mask must be a contiguous [Sq, W] or [B, Sq, W] tensor of q's dtype")
+        bstride = 0 if mask.dim() == 2 else mask.stride(0)
+        if mask.dim() == 3 and mask.shape[0] != B:
+            raise ValueError("a batched mask needs one matrix per batch entry")
+        fa_prefill_mask(q, k, v, mask, mask.shape[-1], bstride, out, lse, B, Hq, Hkv, Sq, Skv, D,
+                        causal, scale, _fa_dtype(q.dtype), _fa_dtype(out.dtype), ws, wsb, stream)
     return (out, lse) if return_lse else out
 
 

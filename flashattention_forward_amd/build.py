@@ -1,7 +1,9 @@
 """Build libfa.so (gfx950 kernels + C-ABI front end) in-tree with hipcc.
 
-Usage: ``python -m flashattention_forward_amd.build`` (or ``build()``). Every
-call recompiles; objects go to ``_build/`` next to this file.
+Usage: ``python flashattention_forward_amd/build.py`` (or ``build()`` of this file
+loaded by path: importing the package itself loads the library, which a build
+must not need). Every call recompiles; objects go to ``_build/`` next to this
+file.
 """
 from __future__ import annotations
 

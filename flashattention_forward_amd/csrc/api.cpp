@@ -197,10 +197,11 @@ size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D,
   return plan_prefill(B, Hq, Sq, Skv, D, true).ws_bytes;
 }
 
-int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
-                  int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
-                  fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
-                  size_t workspace_bytes, hipStream_t stream) {
+static int prefill_impl(const void* q, const void* k, const void* v, const void* mask,
+                        int64_t mask_stride, int64_t mask_bstride, void* o, float* lse, int B,
+                        int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                        fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
+                        size_t workspace_bytes, hipStream_t stream) {
   int rc = check_prefill(q, k, v, o, lse, B, Hq, Hkv, Sq, Skv, D, in_dtype, out_dtype);
   if (rc != FA_OK) return rc;
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
@@ -230,6 +231,9 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
   // Exponent scale; zero is passed as the smallest positive value so that
   // masked scores (-inf) still give probability 0 (and exp2(s * 1e-30) == 1).
   p.scale_log2 = std::max(p.scale * 1.4426950408889634f, 1e-30f);
+  p.mask = mask;
+  p.mask_stride = mask_stride;
+  p.mask_bstride = mask_bstride;
   const int64_t rows = (int64_t)B * Sq * Hq;
   if (pl.n_splits > 1) {
     p.part_o = workspace;
@@ -256,6 +260,29 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
     if (launch_combine(c, ot, stream) != hipSuccess) return FA_ERR_HIP;
   }
   return FA_OK;
+}
+
+int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* lse, int B,
+                  int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                  fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
+                  size_t workspace_bytes, hipStream_t stream) {
+  return prefill_impl(q, k, v, nullptr, 0, 0, o, lse, B, Hq, Hkv, Sq, Skv, D, causal, scale,
+                      in_dtype, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_prefill_mask(const void* q, const void* k, const void* v, const void* mask,
+                    int64_t mask_stride, int64_t mask_batch_stride, void* o, float* lse, int B,
+                    int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                    fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream) {
+  if (!mask) return FA_ERR_NULL;
+  if ((reinterpret_cast<uintptr_t>(mask) & 7u) != 0 || mask_stride % 4 != 0 ||
+      mask_batch_stride % 4 != 0)
+    return FA_ERR_ALIGN;
+  if (mask_stride < ((int64_t)Skv + 3) / 4 * 4 || mask_batch_stride < 0) return FA_ERR_SHAPE;
+  return prefill_impl(q, k, v, mask, mask_stride, mask_batch_stride, o, lse, B, Hq, Hkv, Sq,
+                      Skv, D, causal, scale, in_dtype, out_dtype, workspace, workspace_bytes,
+                      stream);
 }
 
 int fa_prefill(const void* q, const void* k, const void* v, void* o, int B, int Hq, int Hkv,

@@ -27,6 +27,11 @@ struct PrefillParams {
   int q_neg;     // 1: the scale was negative; the kernel uses -Q and |scale|
   float scale;       // |scale|, multiplies q.k
   float scale_log2;  // |scale| * log2(e)
+  // Explicit additive mask (input type) or null: element (b, i, j) at
+  // mask[b * mask_bstride + i * mask_stride + j]; mask_stride and mask_bstride
+  // are multiples of 4 and rows hold at least Skv rounded up to 4 elements.
+  const void* mask;
+  int64_t mask_bstride, mask_stride;
 };
 
 // Paged decode, separate K/V pool [P, 2, Hkv, page, D] (D = 128).

@@ -40,7 +40,13 @@
 //    running max moves only when it grows by more than 2^8, so the O
 //    accumulators are rarely rescaled;
 //  * a workgroup may process one of several key splits; it then writes its
-//    normalised partial O and log-sum-exp for a separate combine kernel.
+//    normalised partial O and log-sum-exp for a separate combine kernel;
+//  * with an explicit additive mask (the KQ mask that the same llama.cpp page
+//    counts as memory traffic) every lane loads the 16 mask values of its
+//    query row for each 32-key block one tile ahead (8-byte loads from L2,
+//    into registers) and the scores are taken to the exponent's base-2 domain
+//    as fma(s, scale log2 e, mask log2 e) before the row max, so the running
+//    max, rescale and exponent work unchanged with a unit exponent scale.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -58,7 +64,7 @@ template <int D, int NW_> struct PfCfg {
   static constexpr int BPW = 8 * NCB / NW;    // 1 KB blocks of a tile each wave copies
 };
 
-template <int D, int NW, typename TI, typename TO, bool CAUSAL>
+template <int D, int NW, typename TI, typename TO, bool CAUSAL, bool AMASK>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   using C = PfCfg<D, NW>;
   using T = in_traits<TI>;
@@ -156,8 +162,43 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
   float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = p.scale_log2;
+  // With a mask the scores are already in the base-2 exponent domain.
+  const float sl2 = AMASK ? 1.f : p.scale_log2;
   const int q_last_wave = min(qw0 + 31, p.Sq - 1);
+
+  // Mask values of this lane's query row (rows past the end read the last
+  // row): chunk m of a tile holds keys k0 + 8 m + 4 h .. + 3, i.e. the four
+  // scores 4 (m & 3) .. + 3 of score block m >> 2. A chunk at or past the end
+  // of the keys reads chunk 0 instead (those keys are masked anyway).
+  u32x2 mk[8];
+  const char* mrow = nullptr;
+  if constexpr (AMASK)
+    mrow = (const char*)p.mask +
+           ((int64_t)b * p.mask_bstride + (int64_t)min(qi, p.Sq - 1) * p.mask_stride) * 2;
+  auto load_mask = [&](int t) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m) {
+      const int kk = t * PF_BN + 8 * m + 4 * h;
+      mk[m] = *(const u32x2*)(mrow + (kk < p.Skv ? kk : 0) * 2);
+    }
+  };
+  // Scores of the tile into the exponent domain: s * scale log2 e + mask log2 e.
+  auto add_mask = [&](f32x16 (&sacc)[2]) {
+    constexpr float LOG2E = 1.4426950408889634f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t w2 = mk[4 * kb + (i >> 2)][(i >> 1) & 1];
+        const uint16_t bits = (i & 1) ? (uint16_t)(w2 >> 16) : (uint16_t)w2;
+        float mv;
+        if constexpr (std::is_same<TI, bf16_t>::value)
+          mv = __uint_as_float((uint32_t)bits << 16);
+        else
+          mv = (float)__builtin_bit_cast(_Float16, bits);
+        sacc[kb][i] = fmaf(sacc[kb][i], p.scale_log2, mv * LOG2E);
+      }
+  };
 
   // Per-lane LDS offsets (blk_slot written out). K (A operand): row 32 kb + c,
   // chunk 2s + h; the offset alternates with the parity of s.
@@ -322,6 +363,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   f32x16 sA[2], sB[2];
   float mx_pend = -INFINITY;
   if (t_begin < t_end) {
+    if constexpr (AMASK) load_mask(t_begin);
     issue_k(t_begin);
     wait_vmcnt<0>();
     lds_barrier();
@@ -334,13 +376,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     constexpr bool MASK = decltype(mask_tag)::value;
     wait_vmcnt<0>();
     lds_barrier();
+    // (The mask values are used before any copy is issued: the compiler's own
+    // wait for them counts no inline-assembly copies and would be a full wait.)
+    if constexpr (AMASK) add_mask(cur);
     if (t + 2 < t_end) issue_k(t + 2);
     if (t + 1 < t_end) issue_v(t + 1);
+    if constexpr (AMASK)
+      if (t + 1 < t_end) load_mask(t + 1);
     // After the last tile the block still computes scores from a stale K stage
     // (in bounds, never used): that keeps the block free of branches.
     // A tile wholly above this wave's causal diagonal is masked out entirely
     // (every probability 0); it runs through the same block.
-    const float mx = MASK ? apply_mask(cur, t * PF_BN) : mx_pend;
+    const float mx = MASK ? apply_mask(cur, t * PF_BN) : AMASK ? tile_max(cur) : mx_pend;
     const float nb = rescale(mx);
     body(cur, nxt, smem + k_stage(t + 1), smem + v_stage(t), nb, mx_pend);
   };
@@ -367,7 +414,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   const float l_tot = sum_xor32(l_run);
   if (!q_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
+  // (With a mask m_run is in the base-2 domain.)
+  const float lse = l_tot > 0.f ? (AMASK ? m_run * 0.6931471805599453f : m_run * p.scale) +
+                                      __logf(l_tot)
+                                : -INFINITY;
   // The output row, or with several splits this split's partial row (in the
   // output's type; the combine weighs the partials by their lse).
   const int64_t row = ((int64_t)b * p.Sq + qi) * p.Hq + hq;
@@ -394,10 +444,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 template <int D, int NW, typename TI, typename TO>
 static hipError_t launch4(const PrefillParams& p, bool causal, hipStream_t stream) {
   const int n = p.B * p.Hq * p.n_qtiles * p.n_splits;
-  if (causal)
-    hipLaunchKernelGGL((prefill_kernel<D, NW, TI, TO, true>), dim3(n), dim3(64 * NW), 0, stream, p);
+  auto go = [&](auto kern) { hipLaunchKernelGGL(kern, dim3(n), dim3(64 * NW), 0, stream, p); };
+  if (p.mask)
+    causal ? go(prefill_kernel<D, NW, TI, TO, true, true>)
+           : go(prefill_kernel<D, NW, TI, TO, false, true>);
   else
-    hipLaunchKernelGGL((prefill_kernel<D, NW, TI, TO, false>), dim3(n), dim3(64 * NW), 0, stream, p);
+    causal ? go(prefill_kernel<D, NW, TI, TO, true, false>)
+           : go(prefill_kernel<D, NW, TI, TO, false, false>);
   return hipGetLastError();
 }
 
@@ -420,7 +473,8 @@ static hipError_t launch2(const PrefillParams& p, OutType ot, bool causal, hipSt
 
 hipError_t launch_prefill(const PrefillParams& p, int D, InType it, OutType ot, bool causal,
                           hipStream_t stream) {
-  if (D == 128 && p.waves == 8 && p.pingpong) return launch_prefill_pp(p, it, ot, causal, stream);
+  if (D == 128 && p.waves == 8 && p.pingpong && !p.mask)
+    return launch_prefill_pp(p, it, ot, causal, stream);
   if (D == 64)
     return it == InType::bf16 ? launch2<64, bf16_t>(p, ot, causal, stream)
                               : launch2<64, f16_t>(p, ot, causal, stream);

@@ -99,6 +99,31 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
                   fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
                   size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Prefill attention with an explicit additive mask:
+ *     O = softmax(scale * Q K^T + M) V        (and the causal rule if causal)
+ * The mask is the KQ mask of "CUDA: fix FA occupancy, optimize tile kernel"
+ * (llama.cpp, opening paragraph), one matrix per batch entry or shared:
+ *   mask               element (b, i, j) at mask[b * mask_batch_stride +
+ *                      i * mask_stride + j], in in_dtype; finite or -inf (-inf
+ *                      hides the key; a row whose keys are all hidden gives
+ *                      o = 0 and lse = -inf). mask_batch_stride 0 shares one
+ *                      [Sq, Skv] mask over the batch.
+ *   mask_stride        elements between rows: a multiple of 4 and at least Skv
+ *                      rounded up to 4 (the kernel reads keys in groups of 4;
+ *                      entries past Skv are read but never used)
+ *   mask_batch_stride  0, or elements between batch entries (a multiple of 4)
+ * The mask pointer must be 8-byte aligned (FA_ERR_ALIGN otherwise); a null mask
+ * is FA_ERR_NULL. Every other argument is as for fa_prefill_ex. The mask is read
+ * from device memory by every query head (it is small against K and V and
+ * stays in L2).
+ */
+int fa_prefill_mask(const void* q, const void* k, const void* v, const void* mask,
+                    int64_t mask_stride, int64_t mask_batch_stride, void* o, float* lse, int B,
+                    int Hq, int Hkv, int Sq, int Skv, int D, int causal, float scale,
+                    fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
+                    size_t workspace_bytes, hipStream_t stream);
+
 /* Bytes of workspace the planner may use for this prefill shape (0 if it never
  * splits it). Pure host function: needs no GPU. Environment variable
  * FA_PREFILL_SPLITS forces a split count (tuning); FA_NUM_CUS sets the compute

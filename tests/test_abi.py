@@ -25,8 +25,8 @@ def declared_functions():
 
 def test_header_declares_entry_points():
     names = declared_functions()
-    for n in ["fa_prefill", "fa_prefill_ex", "fa_decode_paged", "fa_prefill_workspace_size",
-              "fa_decode_workspace_size", "fa_strerror"]:
+    for n in ["fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_decode_paged",
+              "fa_prefill_workspace_size", "fa_decode_workspace_size", "fa_strerror"]:
         assert n in names
 
 
@@ -51,6 +51,19 @@ def _err(fn, *a, **k):
 
 
 A = 1 << 20  # a 16-byte aligned fake address: never dereferenced by these calls
+
+
+def test_prefill_mask_validation(fa):
+    def call(mask=A, stride=16, bstride=0, Skv=13):
+        return fa.fa_prefill_mask(A, A, A, mask, stride, bstride, A, None, 1, 4, 2, 8, Skv, 64, 0,
+                                  0.1, fa.FA_BF16, fa.FA_BF16, None, 0, stream=0)
+
+    assert _err(call, mask=None) == -1
+    assert _err(call, mask=A + 4) == -4  # mask rows are read 8 bytes at a time
+    assert _err(call, stride=18) == -4
+    assert _err(call, bstride=6) == -4
+    assert _err(call, stride=12) == -2  # Skv = 13 needs rows of >= 16 elements
+    assert _err(call, bstride=-4) == -2
 
 
 def test_prefill_validation(fa):

@@ -40,7 +40,7 @@ def check(fa, inp, what, num_splits=0, batches=None):
     ref, ref_lse = oracle.decode_paged(inp, batches)
     sel = slice(None) if batches is None else list(batches)
     assert_parity(o[sel], ref, inp.dtype, what)
-    assert_lse(lse[sel], ref_lse, what)
+    assert_lse(lse[sel], ref_lse, what, dtype=inp.dtype)
     return o, lse
 
 

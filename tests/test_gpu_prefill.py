@@ -65,7 +65,7 @@ def test_prefill_small_parity(fa, shape):
     o, lse = run(fa, inp)
     ref, ref_lse = oracle.prefill(inp)
     assert_parity(to_f64(o), ref, it, f"prefill {shape}")
-    assert_lse(to_f64(lse), ref_lse, f"prefill {shape}")
+    assert_lse(to_f64(lse), ref_lse, f"prefill {shape}", dtype=it)
     if causal and Sq > Skv:
         assert np.all(to_f64(o)[:, :Sq - Skv] == 0.0)
 
@@ -78,7 +78,7 @@ def test_tiny_causal_fp16_fp32_out(fa):
     ref, ref_lse = oracle.prefill(inp)
     assert o.dtype.itemsize == 4
     assert_parity(to_f64(o), ref, "fp16", "workload 1")
-    assert_lse(to_f64(lse), ref_lse, "workload 1")
+    assert_lse(to_f64(lse), ref_lse, "workload 1", dtype="fp16")
 
 
 @pytest.mark.parametrize("splits", ["none", "1", "2", "4", "8", "auto"])
@@ -206,3 +206,98 @@ def test_gqa_ubatch_full_size_sampled(fa):
     full, _ = fa.prefill(q, k, v, causal=True, scale=inp.scale, return_lse=True)
     torch.cuda.synchronize()
     assert_parity(of, to_f64(full), "bf16", "workload 3 ubatches vs one call")
+
+
+# --------------------------------------------------------------------------
+# explicit additive mask (fa_prefill_mask)
+# --------------------------------------------------------------------------
+
+def run_masked(fa, inp, *, stride_pad=0):
+    """Runs fa.prefill with inp.mask (bits [Bm, Sq, W]); W is the mask's own
+    row stride (Skv rounded up to 4 plus padding, NaN-poisoned past Skv)."""
+    import torch
+    q, k, v = (to_dev(x, inp.in_dtype) for x in (inp.q, inp.k, inp.v))
+    m = to_dev(inp.mask, inp.in_dtype)
+    if m.shape[0] == 1:
+        m = m[0]
+    res = fa.prefill(q, k, v, causal=inp.causal, scale=inp.scale,
+                     out_dtype=_dtype_torch(inp.out_dtype), return_lse=True, mask=m)
+    torch.cuda.synchronize()
+    return res
+
+
+def _mask_inputs(c, shape, kind, batched=False, pad=0):
+    B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
+    inp = fi.prefill_inputs(c, B, Hq, Hkv, Sq, Skv, D, causal, it, ot)
+    stride = (Skv + 3) // 4 * 4 + pad
+    return fi.with_mask(inp, c, kind, batched=batched, stride=stride)
+
+
+MASK_SHAPES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, in, out
+    (1, 4, 2, 200, 333, 128, False, "bf16", "bf16"),
+    (1, 4, 2, 200, 333, 128, True, "bf16", "bf16"),
+    (2, 4, 4, 130, 67, 64, False, "fp16", "fp16"),
+    (1, 2, 1, 96, 250, 64, True, "bf16", "fp32"),
+    (1, 32, 8, 512, 1536, 128, True, "bf16", "bf16"),  # 8-wave workgroups, split keys
+]
+
+
+@pytest.mark.parametrize("kind", ["normal", "packed", "bias", "rows"])
+@pytest.mark.parametrize("shape", MASK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_mask_parity(fa, shape, kind):
+    """softmax(scale Q K^T + M) V for random, packed-sequence, distance-bias and
+    hidden-row masks (one shared [Sq, W] matrix, W padded with NaN past Skv)."""
+    log(f"prefill mask {kind} {shape}")
+    inp = _mask_inputs(60, shape, kind, pad=4)
+    o, lse = run_masked(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, shape[7], f"mask {kind} {shape}")
+    assert_lse(to_f64(lse), ref_lse, f"mask {kind} {shape}", dtype=shape[7])
+    if kind == "rows":  # fully hidden rows give exactly 0 and -inf
+        hidden = np.isneginf(ref_lse)
+        assert hidden.any() and np.all(to_f64(o).transpose(0, 2, 1, 3)[hidden] == 0)
+
+
+def test_prefill_mask_batched_and_scales(fa):
+    """One mask per batch entry; scale 0 (softmax of the mask alone) and a
+    negative scale."""
+    shape = (3, 4, 2, 100, 150, 128, False, "bf16", "bf16")
+    for scale in (None, 0.0, -0.07):
+        inp = _mask_inputs(61, shape, "normal", batched=True)
+        if scale is not None:
+            inp.scale = fi.f32(scale)
+        log(f"prefill batched mask scale={inp.scale}")
+        o, lse = run_masked(fa, inp)
+        ref, ref_lse = oracle.prefill(inp)
+        assert_parity(to_f64(o), ref, "bf16", f"batched mask scale={inp.scale}")
+        assert_lse(to_f64(lse), ref_lse, f"batched mask scale={inp.scale}")
+
+
+@pytest.mark.parametrize("waves,splits", [("4", "1"), ("4", "4"), ("8", "1"), ("8", "3")])
+def test_prefill_mask_waves_and_splits(fa, waves, splits, monkeypatch):
+    """Both workgroup shapes and forced split counts with a mask (the split
+    partials carry base-2 maxima through the lse)."""
+    monkeypatch.setenv("FA_PREFILL_WAVES", waves)
+    monkeypatch.setenv("FA_PREFILL_SPLITS", splits)
+    shape = (1, 4, 2, 600, 2000, 128, True, "bf16", "bf16")
+    inp = _mask_inputs(62, shape, "bias")
+    log(f"prefill mask waves={waves} splits={splits}")
+    o, lse = run_masked(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, "bf16", f"mask waves={waves} splits={splits}")
+    assert_lse(to_f64(lse), ref_lse, f"mask waves={waves} splits={splits}")
+
+
+def test_prefill_zero_mask_equals_unmasked(fa):
+    """An all-zero mask gives the unmasked kernel's result up to the one extra
+    rounding of the exponent argument."""
+    import torch
+    shape = (1, 8, 2, 300, 700, 128, True, "bf16", "bf16")
+    inp = fi.prefill_inputs(63, *shape)
+    q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    zero = torch.zeros((300, 700), dtype=torch.bfloat16, device=q.device)
+    o0 = fa.prefill(q, k, v, causal=True, scale=inp.scale)
+    o1 = fa.prefill(q, k, v, causal=True, scale=inp.scale, mask=zero)
+    torch.cuda.synchronize()
+    assert_parity(to_f64(o1), to_f64(o0).astype(np.float64), "bf16", "zero mask vs none")
