@@ -119,6 +119,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
+    ap.add_argument("--no-mask", action="store_true",
+                    help="skip the masked-prefill measurement (fa_prefill_mask)")
     ap.add_argument("--traffic", action="store_true",
                     help="run only the launches that the HBM-traffic counter runs measure: a "
                          "256 MiB device copy (calibration), the last prefill microbatch "
@@ -176,6 +178,17 @@ def main():
             fa.fa_prefill_ex(q, k, v, o, None, 1, Hq, Hkv, UB, skv, D, 1, inp3.scale,
                              fa.FA_BF16, fa.FA_BF16, ws3, ws3_bytes, stream=sid)
 
+    # The same 32 microbatches with an explicit additive mask (a distance bias,
+    # slope 1/8, with -inf above the causal diagonal; the causal rule is on too).
+    masks3 = None
+    if not args.no_mask and not args.traffic:
+        masks3 = [to_dev(fi.bias_mask(UB, UB * (u + 1), 3)) for u in range(n_ub)]
+
+    def prefill_mask_pass():
+        for (q, k, v, o, skv), m in zip(ub_args, masks3):
+            fa.fa_prefill_mask(q, k, v, m, skv, 0, o, None, 1, Hq, Hkv, UB, skv, D, 1,
+                               inp3.scale, fa.FA_BF16, fa.FA_BF16, ws3, ws3_bytes, stream=sid)
+
     def decode_pass():
         fa.fa_decode_paged(q4, pool4, pool4.shape[0], pt4, sl4, o4, None, inp4.B, inp4.Hq, 1, 576,
                            512, 1, inp4.max_pages, inp4.max_seq_len, fa.FA_KV_MLA_SHARED,
@@ -216,6 +229,19 @@ def main():
         step(e)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+
+    t_pfm = None
+    if masks3 is not None:
+        for _ in range(2):
+            prefill_mask_pass()
+        ev_m = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                for _ in range(args.steps)]
+        for e0, e1 in ev_m:
+            e0.record(stream)
+            prefill_mask_pass()
+            e1.record(stream)
+        torch.cuda.synchronize()
+        t_pfm = sum(e0.elapsed_time(e1) for e0, e1 in ev_m) / 1e3
 
     t_pf = sum(e[0].elapsed_time(e[1]) for e in events) / 1e3  # s
     t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / 1e3
@@ -283,6 +309,26 @@ def main():
         },
         "cpu_baseline": None,
     }
+    if t_pfm is not None:
+        pfm_tflops = flops3 * K / t_pfm / 1e12
+        result["prefill_mask"] = {
+            "metric": "masked prefill attn TFLOP/s (%MFMA peak)",
+            "value": round(pfm_tflops, 2),
+            "unit": "TFLOP/s",
+            "ms_per_pass": round(t_pfm / K * 1e3, 4),
+            "mask": "explicit additive [512, keys] bf16 mask per microbatch: distance bias "
+                    "-(p_i - j)/8, -inf above the causal diagonal; causal rule also on",
+            "roofline": {
+                "bound": "mfma",
+                "achieved": round(pfm_tflops, 2),
+                "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s",
+                "frac": round(pfm_tflops / PEAK_BF16_TFLOPS, 4),
+                "traffic": None,
+                "kernel": "fa_prefill_mask call (masked prefill kernel + split combine), "
+                          "averaged over the 32 microbatch launches",
+            },
+        }
     if args.cpu_budget > 0:
         eprint("timing the CPU oracle baseline ...")
         result["cpu_baseline"] = cpu_baseline(inp3, args.cpu_budget)

@@ -181,6 +181,24 @@ def additive_mask(c: int, Bm: int, Sq: int, Skv: int, kind: str, dtype: str = BF
     return bits
 
 
+def bias_mask(Sq: int, Skv: int, e: int, dtype: str = BF16, stride: Optional[int] = None,
+              block: int = 512) -> np.ndarray:
+    """uint16 bits [Sq, stride] of the ``bias`` kind of ``additive_mask`` with a
+    given exponent e (value -2^-e (p_i - j) for j <= p_i, -inf beyond; NaN past
+    Skv), built a block of rows at a time so that large masks stay cheap."""
+    stride = Skv if stride is None else stride
+    assert stride >= Skv
+    out = np.full((Sq, stride), NAN_BITS[dtype], dtype=np.uint16)
+    slope = np.float32(2.0 ** -e)
+    key = np.arange(Skv, dtype=np.int64)[None, :]
+    for r0 in range(0, Sq, block):
+        pos = (Skv - Sq + np.arange(r0, min(r0 + block, Sq), dtype=np.int64))[:, None]
+        d = (pos - key).astype(np.float32)
+        x = np.where(d >= 0, -slope * d, np.float32(-np.inf))  # -inf rounds to -inf
+        out[r0:r0 + len(pos), :Skv] = round_bits(x, dtype)
+    return out
+
+
 def with_mask(inp: PrefillInputs, c: int, kind: str, batched: bool = False,
               stride: Optional[int] = None) -> PrefillInputs:
     """The same inputs with an additive mask attached (one per batch entry if
