@@ -98,7 +98,7 @@ class PrefillInputs:
 
 @dataclasses.dataclass
 class DecodeInputs:
-    q: np.ndarray  # uint16 bits [B, Hq, D_qk]
+    q: np.ndarray  # uint16 bits [B, Hq, D_qk], or [B, Sq, Hq, D_qk] when Sq > 1
     pool: np.ndarray  # uint16 bits, layout depends on ``layout``
     page_table: np.ndarray  # int32 [B, max_pages]
     seq_lens: np.ndarray  # int32 [B]
@@ -112,6 +112,7 @@ class DecodeInputs:
     layout: str  # "split": [P, 2, Hkv, page, D]; "mla": [P, page, D_qk]
     scale: float
     dtype: str
+    Sq: int = 1  # new tokens per sequence (the last Sq of each sequence)
 
     @property
     def max_pages(self) -> int:
@@ -228,8 +229,10 @@ def mla_decode_inputs(c: int, B: int, Hq: int, seq_len: int, D_qk: int = 576, D_
 
 def split_decode_inputs(c: int, B: int, Hq: int, Hkv: int, D: int, lens, page_size: int,
                         dtype: str = BF16, spare_pages: int = 64,
-                        scale: Optional[float] = None, poison: bool = True) -> DecodeInputs:
-    """Paged decode with separate K and V per (page, head).
+                        scale: Optional[float] = None, poison: bool = True,
+                        Sq: int = 1) -> DecodeInputs:
+    """Paged decode with separate K and V per (page, head); with Sq > 1 the
+    queries are the last Sq tokens of each sequence, q [B, Sq, Hq, D].
 
     Pool layout ``[num_pages, 2 (K, V), Hkv, page_size, D]``. Sequence b owns
     ceil(len_b / page_size) pages drawn from a seeded permutation of the pool;
@@ -242,7 +245,7 @@ def split_decode_inputs(c: int, B: int, Hq: int, Hkv: int, D: int, lens, page_si
     n_pages = int(sum(pages_per)) + spare_pages
     max_len = int(lens.max()) if B else 0
     max_pages = max(1, (max_len + page_size - 1) // page_size)
-    q = normal_bits((B, Hq, D), dtype, rng_for(c, T_Q))
+    q = normal_bits((B, Sq, Hq, D) if Sq > 1 else (B, Hq, D), dtype, rng_for(c, T_Q))
     pool = normal_bits((n_pages, 2, Hkv, page_size, D), dtype, rng_for(c, T_POOL))
     perm = rng_for(c, T_PERM).permutation(n_pages).astype(np.int32)
     page_table = np.full((B, max_pages), -1, dtype=np.int32)
@@ -261,7 +264,7 @@ def split_decode_inputs(c: int, B: int, Hq: int, Hkv: int, D: int, lens, page_si
     if scale is None:
         scale = 1.0 / math.sqrt(D)
     return DecodeInputs(q, pool, page_table, lens.astype(np.int32), B, Hq, Hkv, D, D,
-                        page_size, max_len, "split", f32(scale), dtype)
+                        page_size, max_len, "split", f32(scale), dtype, Sq)
 
 
 def random_lens(c: int, B: int, lo: int, hi: int) -> np.ndarray:

@@ -180,11 +180,16 @@ def gather_paged(pool, page_table, seq_len, page_size, layout, b, Hkv, D_qk, D_v
 
 
 def decode_paged(inp, batches=None, nthreads=None):
-    """Oracle of paged decode (one query token per sequence, no mask).
+    """Oracle of paged decode.
 
-    ``inp`` has q [B, Hq, D_qk] bits, pool bits, page_table, seq_lens, page_size,
-    layout ("split" or "mla"), Hkv, D_qk, D_v, scale and dtype. Returns
-    (o [nb, Hq, D_v], lse [nb, Hq]) for the listed batches (all by default).
+    ``inp`` has q bits, pool bits, page_table, seq_lens, page_size, layout
+    ("split" or "mla"), Hkv, D_qk, D_v, scale, dtype and Sq. With Sq = 1, q is
+    [B, Hq, D_qk], one query token per sequence seeing all its cached tokens,
+    and the result is (o [nb, Hq, D_v], lse [nb, Hq]). With Sq > 1, q is
+    [B, Sq, Hq, D_qk]: the queries are the sequence's last Sq tokens, token i
+    at position seq_len - Sq + i, each seeing the tokens up to its own position
+    (the bottom-right causal rule of the prefill reading); the result is
+    (o [nb, Sq, Hq, D_v], lse [nb, Hq, Sq]). Listed batches, all by default.
     """
     if batches is None:
         batches = range(inp.B)
@@ -195,7 +200,12 @@ def decode_paged(inp, batches=None, nthreads=None):
     for b in batches:
         K, V = gather_paged(pool, inp.page_table, inp.seq_lens[b], inp.page_size, inp.layout, b,
                             inp.Hkv, inp.D_qk, inp.D_v)
-        o, lse = attention(q[b][None, None], K, V, False, float(inp.scale), nthreads)
-        outs.append(o[0, 0])
-        lses.append(lse[0, :, 0])
+        if getattr(inp, "Sq", 1) > 1:
+            o, lse = attention(q[b][None], K, V, True, float(inp.scale), nthreads)
+            outs.append(o[0])
+            lses.append(lse[0])
+        else:
+            o, lse = attention(q[b][None, None], K, V, False, float(inp.scale), nthreads)
+            outs.append(o[0, 0])
+            lses.append(lse[0, :, 0])
     return np.stack(outs), np.stack(lses)

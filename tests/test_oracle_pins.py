@@ -374,6 +374,59 @@ def test_paged_split_equals_contiguous(oracle_lib, page_size):
         assert np.all(np.isfinite(o[b]))
 
 
+@pytest.mark.parametrize("page_size", [1, 4])
+def test_paged_multi_token_matches_torch_sdpa(oracle_lib, page_size):
+    """Sq new tokens per sequence over a paged pool: against torch float64 SDPA
+    with its own lower-right causal bias on the K/V scattered into the pool
+    (the pool is built independently of the oracle's gather)."""
+    r = np.random.default_rng(40 + page_size)
+    B, Hkv, G, D, Sq = 3, 2, 3, 5, 4
+    lens = [9, 4, 13]
+    K = [r.standard_normal((n, Hkv, D)) for n in lens]
+    V = [r.standard_normal((n, Hkv, D)) for n in lens]
+    pool, table = _scatter_split_pool(K, V, page_size, r)
+    d = _Dec()
+    d.q = r.standard_normal((B, Sq, Hkv * G, D)); d.pool = pool; d.page_table = table
+    d.seq_lens = np.array(lens, dtype=np.int32); d.page_size = page_size; d.layout = "split"
+    d.Hkv = Hkv; d.D_qk = D; d.D_v = D; d.scale = 0.6; d.dtype = "fp64"; d.B = B; d.Sq = Sq
+    o, lse = oracle.decode_paged(d)
+    assert o.shape == (B, Sq, Hkv * G, D) and lse.shape == (B, Hkv * G, Sq)
+    for b in range(B):
+        ref = _sdpa(d.q[b][None], K[b][None], V[b][None], True, 0.6)
+        np.testing.assert_allclose(o[b], ref[0], rtol=1e-12, atol=1e-12)
+
+
+def test_paged_multi_token_is_truncated_single_token(oracle_lib):
+    """New token i of Sq equals a one-token decode of the same sequence cut to
+    its first seq_len - Sq + i + 1 tokens; a token whose position is negative
+    (seq_len < Sq) sees nothing."""
+    r = np.random.default_rng(44)
+    B, Hkv, G, D, Sq = 2, 1, 2, 3, 5
+    lens = [8, 3]
+    K = [r.standard_normal((n, Hkv, D)) for n in lens]
+    V = [r.standard_normal((n, Hkv, D)) for n in lens]
+    pool, table = _scatter_split_pool(K, V, 2, r)
+    d = _Dec()
+    d.q = r.standard_normal((B, Sq, Hkv * G, D)); d.pool = pool; d.page_table = table
+    d.seq_lens = np.array(lens, dtype=np.int32); d.page_size = 2; d.layout = "split"
+    d.Hkv = Hkv; d.D_qk = D; d.D_v = D; d.scale = 1.1; d.dtype = "fp64"; d.B = B; d.Sq = Sq
+    o, lse = oracle.decode_paged(d)
+    for b in range(B):
+        for i in range(Sq):
+            n = lens[b] - Sq + i + 1
+            if n <= 0:
+                assert np.all(o[b, i] == 0) and np.all(np.isneginf(lse[b, :, i]))
+                continue
+            e = _Dec()
+            e.__dict__.update(d.__dict__)
+            e.Sq = 1
+            e.q = d.q[:, i]
+            e.seq_lens = np.array([n if bb == b else 1 for bb in range(B)], dtype=np.int32)
+            o1, l1 = oracle.decode_paged(e, [b])
+            np.testing.assert_array_equal(o[b, i], o1[0])
+            np.testing.assert_array_equal(lse[b, :, i], l1[0])
+
+
 def test_paged_zero_length_sequence(oracle_lib):
     d = _Dec()
     d.q = _rand(1, 2, 4); d.pool = np.full((2, 2, 1, 4, 4), np.nan)
