@@ -61,6 +61,16 @@ def decode_bytes(inp):
     return kv + q + o + pt + inp.B * 4
 
 
+def split_decode_bytes(inp):
+    """Algorithmic bytes of paged GQA decode: K and V rows of every cached token once
+    per K/V head, q and o of the Sq new tokens, the page-table entries used and the lengths."""
+    kv = int(inp.seq_lens.astype("int64").sum()) * inp.Hkv * 2 * inp.D_qk * 2
+    q = inp.B * inp.Sq * inp.Hq * inp.D_qk * 2
+    o = inp.B * inp.Sq * inp.Hq * inp.D_v * 2
+    pt = int(sum((int(n) + inp.page_size - 1) // inp.page_size for n in inp.seq_lens)) * 4
+    return kv + q + o + pt + inp.B * 4
+
+
 def source_sha(*names):
     h = hashlib.sha256()
     for n in names:
@@ -189,6 +199,23 @@ def main():
             fa.fa_prefill_mask(q, k, v, m, skv, 0, o, None, 1, Hq, Hkv, UB, skv, D, 1,
                                inp3.scale, fa.FA_BF16, fa.FA_BF16, ws3, ws3_bytes, stream=sid)
 
+    # Workload 5's small batch (4 sequences of 1024..32768 tokens, 32 query / 8 K/V
+    # heads, page 16) decoding 4 new tokens per sequence at once.
+    inp5 = fi.split_decode_inputs(5, 4, 32, 8, 128, fi.random_lens(5, 4, 1024, 32768), 16, Sq=4)
+    q5, pool5 = to_dev(inp5.q), to_dev(inp5.pool)
+    pt5 = torch.from_numpy(inp5.page_table).to(dev)
+    sl5 = torch.from_numpy(inp5.seq_lens).to(dev)
+    o5 = torch.empty((inp5.B, inp5.Sq, inp5.Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws5_bytes = fa.fa_decode_multi_workspace_size(inp5.B, inp5.Sq, inp5.Hq, inp5.Hkv, 128, 128,
+                                                  16, inp5.max_seq_len, fa.FA_KV_SPLIT)
+    ws5 = torch.empty(max(ws5_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
+
+    def decode_multi_pass():
+        fa.fa_decode_paged_multi(q5, pool5, pool5.shape[0], pt5, sl5, o5, None, inp5.B, inp5.Sq,
+                                 inp5.Hq, inp5.Hkv, 128, 128, 16, inp5.max_pages,
+                                 inp5.max_seq_len, fa.FA_KV_SPLIT, inp5.scale, 0, fa.FA_BF16,
+                                 ws5, ws5_bytes, stream=sid)
+
     def decode_pass():
         fa.fa_decode_paged(q4, pool4, pool4.shape[0], pt4, sl4, o4, None, inp4.B, inp4.Hq, 1, 576,
                            512, 1, inp4.max_pages, inp4.max_seq_len, fa.FA_KV_MLA_SHARED,
@@ -242,6 +269,19 @@ def main():
             e1.record(stream)
         torch.cuda.synchronize()
         t_pfm = sum(e0.elapsed_time(e1) for e0, e1 in ev_m) / 1e3
+
+    for _ in range(2):
+        decode_multi_pass()
+    ev_d5 = []
+    for _ in range(args.steps):
+        flush_sum = flush.sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        decode_multi_pass()
+        e1.record(stream)
+        ev_d5.append((e0, e1))
+    torch.cuda.synchronize()
+    t_d5 = sum(e0.elapsed_time(e1) for e0, e1 in ev_d5) / 1e3
 
     t_pf = sum(e[0].elapsed_time(e[1]) for e in events) / 1e3  # s
     t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / 1e3
@@ -308,6 +348,28 @@ def main():
             "tflops": round(36507222016 * K / t_dec / 1e12, 1),
         },
         "cpu_baseline": None,
+    }
+    bytes5 = split_decode_bytes(inp5)
+    d5_gbs = bytes5 * K / t_d5 / 1e9
+    result["decode_multi"] = {
+        "metric": "paged GQA decode of 4 new tokens per sequence GB/s (%HBM peak)",
+        "value": round(d5_gbs, 1),
+        "unit": "GB/s",
+        "us_per_call": round(t_d5 / K * 1e6, 2),
+        "bytes_per_call": bytes5,
+        "workload": "4 sequences of U[1024, 32768] tokens (seeded), 32 query / 8 K/V heads, "
+                    "D=128, page 16, 4 new tokens each (causal among themselves), bf16; "
+                    "cold (after a cache-evicting read)",
+        "splits": max(1, ws5_bytes // (inp5.B * inp5.Sq * inp5.Hq * (128 * 2 + 4))),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(d5_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(d5_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "fa_decode_paged_multi call (GQA decode kernel + split combine)",
+        },
     }
     if t_pfm is not None:
         pfm_tflops = flops3 * K / t_pfm / 1e12

@@ -1,8 +1,9 @@
 """Fused attention forward for AMD MI355X (gfx950): Python binding of libfa.so.
 
 The functions named like the C entry points (``fa_prefill``, ``fa_prefill_ex``,
-``fa_prefill_mask``, ``fa_decode_paged``, the workspace-size queries, ``fa_strerror``) marshal their
-arguments and call the library; every step of the computation runs in the HIP
+``fa_prefill_mask``, ``fa_decode_paged``, ``fa_decode_paged_multi``, the
+workspace-size queries, ``fa_strerror``) marshal their arguments and call the
+library; every step of the computation runs in the HIP
 kernels. torch is used only for device memory and streams. ``prefill`` and
 ``decode_paged`` are conveniences that allocate outputs and workspace with torch
 and then call the same entry points.
@@ -21,7 +22,7 @@ from typing import Optional
 __all__ = [
     "FA_BF16", "FA_FP16", "FA_FP32", "FA_KV_SPLIT", "FA_KV_MLA_SHARED", "FaError",
     "fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_prefill_workspace_size",
-    "fa_decode_paged",
+    "fa_decode_paged", "fa_decode_paged_multi", "fa_decode_multi_workspace_size",
     "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "fa_version",
     "prefill", "decode_paged", "LIB_PATH",
 ]
@@ -37,7 +38,8 @@ if not os.path.exists(LIB_PATH):
 
 _lib = ctypes.CDLL(LIB_PATH)
 for _name in ("fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_prefill_workspace_size",
-              "fa_decode_paged", "fa_decode_workspace_size", "fa_decode_num_splits",
+              "fa_decode_paged", "fa_decode_paged_multi", "fa_decode_multi_workspace_size",
+              "fa_decode_workspace_size", "fa_decode_num_splits",
               "fa_strerror", "fa_version"):
     if not hasattr(_lib, _name):
         raise ImportError(f"{LIB_PATH} lacks {_name} (older than its sources); {_BUILD_HINT}")
@@ -60,6 +62,11 @@ _lib.fa_prefill_workspace_size.restype = _Z
 _lib.fa_decode_paged.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                  _I, _I, _P, _Z, _P]
 _lib.fa_decode_paged.restype = _I
+_lib.fa_decode_paged_multi.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                       _I, _I, _I, _F, _I, _I, _P, _Z, _P]
+_lib.fa_decode_paged_multi.restype = _I
+_lib.fa_decode_multi_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]
+_lib.fa_decode_multi_workspace_size.restype = _Z
 _lib.fa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
 _lib.fa_decode_workspace_size.restype = _Z
 _lib.fa_decode_num_splits.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
@@ -155,6 +162,26 @@ def fa_decode_paged(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Hq, 
                                 int(workspace_bytes), _stream(stream)), "fa_decode_paged")
 
 
+def fa_decode_paged_multi(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Sq, Hq, Hkv,
+                          D_qk, D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale,
+                          num_splits, dtype, workspace=None, workspace_bytes=0,
+                          stream=None) -> None:
+    if workspace is not None and not isinstance(workspace, int) and not workspace_bytes:
+        workspace_bytes = workspace.numel() * workspace.element_size()
+    _check(_lib.fa_decode_paged_multi(_ptr(q), _ptr(kv_pool), int(num_pages), _ptr(page_table),
+                                      _ptr(seq_lens), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv, D_qk,
+                                      D_v, page_size, max_pages_per_seq, max_seq_len,
+                                      int(layout), float(scale), int(num_splits), int(dtype),
+                                      _ptr(workspace), int(workspace_bytes), _stream(stream)),
+           "fa_decode_paged_multi")
+
+
+def fa_decode_multi_workspace_size(B, Sq, Hq, Hkv, D_qk, D_v, page_size, max_seq_len, layout,
+                                   num_splits=0) -> int:
+    return int(_lib.fa_decode_multi_workspace_size(B, Sq, Hq, Hkv, D_qk, D_v, page_size,
+                                                   max_seq_len, int(layout), int(num_splits)))
+
+
 def fa_decode_workspace_size(B, Hq, Hkv, D_qk, D_v, page_size, max_seq_len, layout,
                              num_splits=0) -> int:
     return int(_lib.fa_decode_workspace_size(B, Hq, Hkv, D_qk, D_v, page_size, max_seq_len,
@@ -226,9 +253,16 @@ def decode_paged(q, kv_pool, page_table, seq_lens, *, layout: int, scale: float,
                  max_seq_len: int, page_size: int, D_v: Optional[int] = None,
                  num_splits: int = 0, out=None, return_lse: bool = False, workspace=None,
                  stream=None):
-    """Paged decode on torch tensors. q [B, Hq, D_qk]; kv_pool per layout;
-    page_table [B, max_pages] int32; seq_lens [B] int32 (device)."""
+    """Paged decode on torch tensors. q [B, Hq, D_qk], or [B, Sq, Hq, D_qk] for
+    Sq new tokens per sequence (causal, bottom-right; split K/V layout only);
+    kv_pool per layout; page_table [B, max_pages] int32; seq_lens [B] int32
+    (device). o has q's leading shape; lse is [B, Hq] or [B, Hq, Sq]."""
     import torch
+    if q.dim() == 4:
+        return _decode_multi(q, kv_pool, page_table, seq_lens, layout=layout, scale=scale,
+                             max_seq_len=max_seq_len, page_size=page_size, D_v=D_v,
+                             num_splits=num_splits, out=out, return_lse=return_lse,
+                             workspace=workspace, stream=stream)
     B, Hq, D_qk = q.shape
     if layout == FA_KV_MLA_SHARED:
         Hkv = 1
@@ -249,4 +283,25 @@ def decode_paged(q, kv_pool, page_table, seq_lens, *, layout: int, scale: float,
                     _fa_dtype(q.dtype), workspace,
                     0 if workspace is None else workspace.numel() * workspace.element_size(),
                     stream)
+    return (out, lse) if return_lse else out
+
+
+def _decode_multi(q, kv_pool, page_table, seq_lens, *, layout, scale, max_seq_len, page_size,
+                  D_v, num_splits, out, return_lse, workspace, stream):
+    import torch
+    B, Sq, Hq, D_qk = q.shape
+    Hkv = kv_pool.shape[2]
+    D_v = D_qk if D_v is None else D_v
+    if out is None:
+        out = torch.empty((B, Sq, Hq, D_v), dtype=q.dtype, device=q.device)
+    lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
+    if workspace is None:
+        workspace = _workspace(fa_decode_multi_workspace_size(B, Sq, Hq, Hkv, D_qk, D_v, page_size,
+                                                              max_seq_len, layout, num_splits),
+                               q.device)
+    fa_decode_paged_multi(q, kv_pool, kv_pool.shape[0], page_table, seq_lens, out, lse, B, Sq, Hq,
+                          Hkv, D_qk, D_v, page_size, page_table.shape[1], max_seq_len, layout,
+                          scale, num_splits, _fa_dtype(q.dtype), workspace,
+                          0 if workspace is None else workspace.numel() * workspace.element_size(),
+                          stream)
     return (out, lse) if return_lse else out

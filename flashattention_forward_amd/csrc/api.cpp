@@ -104,7 +104,7 @@ struct DecodePlan {
 };
 
 DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_layout layout,
-                       int num_splits, bool allow_split) {
+                       int num_splits, bool allow_split, int Sq = 1) {
   DecodePlan pl;
   const int tiles = std::max(1, ceil_div(max_seq_len, DEC_TILE));
   int64_t units;
@@ -127,7 +127,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
     target = planner_cus();           // one 8-wave workgroup per CU
     if (nh == 64) min_splits = ceil_div(std::max(1, max_seq_len), MLA_MAX_CHUNK);
   } else {
-    pl.n_hblk = ceil_div(Hq / Hkv, 16);
+    pl.n_hblk = ceil_div((Hq / Hkv) * Sq, 16);  // rows: new tokens x heads of a group
     units = (int64_t)B * Hkv * pl.n_hblk;  // one wave per unit
     target = 8 * (int64_t)planner_cus();   // two waves per SIMD
   }
@@ -150,7 +150,7 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
   if (pl.n_splits < 1) pl.n_splits = 1;
   // Partial outputs in the 16-bit input type, fp32 lse.
   if (pl.n_splits > 1)
-    pl.ws_bytes = (size_t)pl.n_splits * B * Hq * ((size_t)D_v * 2 + sizeof(float));
+    pl.ws_bytes = (size_t)pl.n_splits * B * Sq * Hq * ((size_t)D_v * 2 + sizeof(float));
   return pl;
 }
 
@@ -333,21 +333,23 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int D_qk, int D_v, int page_siz
   return plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, true).n_splits;
 }
 
-int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
-                    const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
-                    int B, int Hq, int Hkv,
-                    int D_qk, int D_v, int page_size, int max_pages_per_seq, int max_seq_len,
-                    fa_kv_layout layout, float scale, int num_splits, fa_dtype dtype,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+static int decode_impl(const void* q, const void* kv_pool, int num_pages,
+                       const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                       int B, int Sq, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                       int max_pages_per_seq, int max_seq_len, fa_kv_layout layout, float scale,
+                       int num_splits, fa_dtype dtype, void* workspace, size_t workspace_bytes,
+                       hipStream_t stream) {
   int rc = check_decode(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Hq, Hkv, D_qk, D_v,
                         page_size, max_pages_per_seq, max_seq_len, layout, dtype);
   if (rc != FA_OK) return rc;
+  if (Sq < 1 || Sq > 64) return FA_ERR_SHAPE;
+  if (Sq > 1 && layout != FA_KV_SPLIT) return FA_ERR_UNSUPPORTED;
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
   if (B == 0) return FA_OK;
   const DecodePlan pl =
-      plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, workspace != nullptr);
+      plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, workspace != nullptr, Sq);
   if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
-  const int64_t rows = (int64_t)B * Hq;
+  const int64_t rows = (int64_t)B * Sq * Hq;
   if (rows > INT_MAX) return FA_ERR_SHAPE;
   void* part_o = nullptr;
   float* part_lse = nullptr;
@@ -393,6 +395,7 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     p.part_o = part_o;
     p.part_lse = part_lse;
     p.B = B;
+    p.Sq = Sq;
     p.Hq = Hq;
     p.Hkv = Hkv;
     p.page_size = page_size;
@@ -421,12 +424,44 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
     c.rows = (int)rows;
     c.D = D_v;
     c.n_splits = pl.n_splits;
-    c.Sq = 1;
+    c.Sq = Sq;
     c.Hq = Hq;
     if (launch_combine(c, dtype == FA_BF16 ? OutType::bf16 : OutType::f16, stream) != hipSuccess)
       return FA_ERR_HIP;
   }
   return FA_OK;
+}
+
+int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
+                    const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                    int B, int Hq, int Hkv,
+                    int D_qk, int D_v, int page_size, int max_pages_per_seq, int max_seq_len,
+                    fa_kv_layout layout, float scale, int num_splits, fa_dtype dtype,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, 1, Hq, Hkv, D_qk,
+                     D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale, num_splits,
+                     dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_decode_paged_multi(const void* q, const void* kv_pool, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                          int B, int Sq, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                          int max_pages_per_seq, int max_seq_len, fa_kv_layout layout,
+                          float scale, int num_splits, fa_dtype dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream) {
+  return decode_impl(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Sq, Hq, Hkv, D_qk,
+                     D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale, num_splits,
+                     dtype, workspace, workspace_bytes, stream);
+}
+
+size_t fa_decode_multi_workspace_size(int B, int Sq, int Hq, int Hkv, int D_qk, int D_v,
+                                      int page_size, int max_seq_len, fa_kv_layout layout,
+                                      int num_splits) {
+  (void)D_qk;
+  (void)page_size;
+  if (B < 1 || Sq < 1 || Hq < 1 || Hkv < 1 || Hq % Hkv != 0 || max_seq_len < 0 || D_v < 1)
+    return 0;
+  return plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, true, Sq).ws_bytes;
 }
 
 }  // extern "C"

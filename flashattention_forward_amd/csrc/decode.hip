@@ -14,6 +14,12 @@
 // (ds_read_b64_tr_b16); the contraction index is relabelled so that each lane's
 // 8 keys match its probability registers.
 //
+// Several new tokens per sequence (Sq > 1: speculative or chunked decode) are
+// packed into the MFMA rows with the heads: row r = i * G + h is token i (at
+// position seq_len - Sq + i, so it sees keys up to that position: causal,
+// bottom-right) and head h of the group, and all rows of a unit share each
+// K/V row it loads.
+//
 // Sequences too short to fill the chip are split over several key ranges
 // (split-KV); each split writes a normalised partial O and its log-sum-exp for
 // the combine kernel. Tokens past seq_len, including page slots that hold
@@ -62,17 +68,20 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
   const int b = unit / p.Hkv;
   const int G = p.Hq / p.Hkv;
   const int c16 = lane & 15, gq = lane >> 4;
-  const int hig = hb * 16 + c16;  // head index inside the group
-  const bool hvalid = hig < G;
-  const int hq = g * G + (hvalid ? hig : 0);
+  const int rig = hb * 16 + c16;  // row inside the group: token rig / G, head rig % G
+  const bool hvalid = rig < G * p.Sq;
+  const int tok = hvalid ? rig / G : 0;
+  const int hq = g * G + (hvalid ? rig % G : 0);
 
   const int seq_len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int t0 = split * p.chunk;
   const int t1 = min(t0 + p.chunk, seq_len);
+  const int lim = seq_len - p.Sq + tok;  // last key this row sees
+  const int lim_lo = seq_len - p.Sq;     // the smallest such key over the rows
 
   u32x4 qf[D / 32];
   {
-    const char* qrow = (const char*)p.q + ((int64_t)b * p.Hq + hq) * D * 2;
+    const char* qrow = (const char*)p.q + (((int64_t)b * p.Sq + tok) * p.Hq + hq) * D * 2;
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       qf[s] = hvalid ? ldg16(qrow + (32 * s + 8 * gq) * 2) : u32x4{0, 0, 0, 0};
@@ -169,6 +178,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
         for (int i = 0; i < 4; ++i)
           if (tt + 16 * kb + 4 * gq + i >= t1) sacc[kb][i] = -INFINITY;
     }
+    if (tt + DEC_TILE - 1 > lim_lo) {  // keys past an earlier new token's position
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (tt + 16 * kb + 4 * gq + i > lim) sacc[kb][i] = -INFINITY;
+    }
     float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                      fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
     mx = fmaxf(mx, xor16(mx));
@@ -221,10 +237,11 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
   if (!hvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
-  // The output row, or with several splits this split's partial row (same
-  // 16-bit type; the combine weighs the partials by their lse).
-  const int64_t row = (int64_t)b * p.Hq + hq;
-  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Hq + row;
+  // The output row ([B, Sq, Hq] order), or with several splits this split's
+  // partial row (same 16-bit type; the combine weighs the partials by their
+  // lse and writes lse as [B, Hq, Sq]).
+  const int64_t row = ((int64_t)b * p.Sq + tok) * p.Hq + hq;
+  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Sq * p.Hq + row;
   char* orow = (char*)(S == 1 ? p.o : p.part_o) + prow * D * 2;
 #pragma unroll
   for (int db = 0; db < D / 16; ++db) {
@@ -233,8 +250,12 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
                   T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
     *(u32x2*)(orow + d * 2) = v;
   }
-  float* lrow = S == 1 ? p.lse : p.part_lse;
-  if (lrow && gq == 0) lrow[prow] = lse;
+  if (gq == 0) {
+    if (S > 1)
+      p.part_lse[prow] = lse;
+    else if (p.lse)
+      p.lse[((int64_t)b * p.Hq + hq) * p.Sq + tok] = lse;
+  }
 }
 
 template <typename TI>

@@ -36,16 +36,16 @@ struct PrefillParams {
 
 // Paged decode, separate K/V pool [P, 2, Hkv, page, D] (D = 128).
 struct DecodeSplitParams {
-  const void* q;  // [B, Hq, D]
+  const void* q;  // [B, Sq, Hq, D]
   const void* pool;
   const int32_t* page_table;  // [B, max_pages]
   const int32_t* seq_lens;    // [B]
-  void* o;                    // [B, Hq, D]
-  float* lse;                 // [B, Hq] or null
-  void* part_o;               // [S, B, Hq, D] in the 16-bit input type
-  float* part_lse;            // [S, B, Hq]
-  int B, Hq, Hkv, page_size, max_pages, num_pages, max_seq_len;
-  int n_hblk;    // ceil((Hq / Hkv) / 16) head blocks per K/V head
+  void* o;                    // [B, Sq, Hq, D]
+  float* lse;                 // [B, Hq, Sq] or null
+  void* part_o;               // [S, B, Sq, Hq, D] in the 16-bit input type
+  float* part_lse;            // [S, B, Sq, Hq]
+  int B, Sq, Hq, Hkv, page_size, max_pages, num_pages, max_seq_len;
+  int n_hblk;    // ceil(Sq * (Hq / Hkv) / 16) row blocks per K/V head
   int chunk;     // tokens per split (multiple of 32)
   int n_splits;
   int n_units;   // B * Hkv * n_hblk * n_splits

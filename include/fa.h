@@ -163,6 +163,34 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
                     fa_kv_layout layout, float scale, int num_splits, fa_dtype dtype,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * Paged decode of Sq new tokens per sequence (speculative or chunked decode):
+ * the Sq queries of sequence b are its last Sq tokens, token i at position
+ * seq_lens[b] - Sq + i, and each sees the cached tokens up to its own position
+ * (causal, bottom-right, as in fa_prefill). With Sq = 1 this is
+ * fa_decode_paged. The query tokens of a sequence and the query heads of a
+ * K/V group are packed into the MFMA rows together, so each K/V row is read
+ * once per (sequence, K/V head).
+ *   q   [B, Sq, Hq, D_qk]; o [B, Sq, Hq, D_v]; lse [B, Hq, Sq] fp32 or NULL
+ *   Sq  1 .. 64
+ * FA_KV_SPLIT layout only for Sq > 1 (FA_ERR_UNSUPPORTED otherwise). A row
+ * whose position is negative (seq_lens[b] < Sq) sees no key: o = 0, lse =
+ * -inf. Every other argument is as for fa_decode_paged; the workspace size
+ * comes from fa_decode_multi_workspace_size.
+ */
+int fa_decode_paged_multi(const void* q, const void* kv_pool, int num_pages,
+                          const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+                          int B, int Sq, int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                          int max_pages_per_seq, int max_seq_len, fa_kv_layout layout,
+                          float scale, int num_splits, fa_dtype dtype, void* workspace,
+                          size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of workspace fa_decode_paged_multi may use (0 if it would not split).
+ * Pure host function. */
+size_t fa_decode_multi_workspace_size(int B, int Sq, int Hq, int Hkv, int D_qk, int D_v,
+                                      int page_size, int max_seq_len, fa_kv_layout layout,
+                                      int num_splits);
+
 /* Bytes of workspace fa_decode_paged may use for this shape and split request
  * (0 if it would not split). Pure host function. */
 size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int D_qk, int D_v, int page_size,

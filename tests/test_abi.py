@@ -26,6 +26,7 @@ def declared_functions():
 def test_header_declares_entry_points():
     names = declared_functions()
     for n in ["fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_decode_paged",
+              "fa_decode_paged_multi", "fa_decode_multi_workspace_size",
               "fa_prefill_workspace_size", "fa_decode_workspace_size", "fa_strerror"]:
         assert n in names
 
@@ -64,6 +65,23 @@ def test_prefill_mask_validation(fa):
     assert _err(call, bstride=6) == -4
     assert _err(call, stride=12) == -2  # Skv = 13 needs rows of >= 16 elements
     assert _err(call, bstride=-4) == -2
+
+
+def test_decode_multi_validation(fa):
+    def call(Sq=4, layout=None, Dqk=128, Dv=128, Hkv=2):
+        lay = fa.FA_KV_SPLIT if layout is None else layout
+        return fa.fa_decode_paged_multi(A, A, 8, A, A, A, None, 2, Sq, 8, Hkv, Dqk, Dv, 16, 4, 64,
+                                        lay, 0.1, 0, fa.FA_BF16, None, 0, stream=0)
+
+    assert _err(call, Sq=0) == -2
+    assert _err(call, Sq=65) == -2
+    assert _err(call, layout=fa.FA_KV_MLA_SHARED, Dqk=576, Dv=512, Hkv=1) == -3
+    # rows = new tokens x heads: 4 sequences x 4 tokens x 32 heads of 16-bit partials + fp32 lse
+    ws = fa.fa_decode_multi_workspace_size(4, 4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT, 3)
+    assert ws == 3 * 4 * 4 * 32 * (128 * 2 + 4)
+    assert fa.fa_decode_multi_workspace_size(4, 1, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT,
+                                             3) == \
+        fa.fa_decode_workspace_size(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT, 3)
 
 
 def test_prefill_validation(fa):

@@ -100,6 +100,31 @@ def test_gqa_decode_full_size(fa):
 
 
 # --------------------------------------------------------------------------
+# several new tokens per sequence (fa_decode_paged_multi)
+# --------------------------------------------------------------------------
+
+@pytest.mark.parametrize("Sq,G,page_size", [(2, 4, 16), (4, 1, 16), (7, 8, 5), (16, 4, 1),
+                                            (64, 2, 16), (5, 16, 16)])
+def test_gqa_decode_multi_token(fa, Sq, G, page_size):
+    """Sq new tokens packed with the group's heads into the MFMA rows; lengths
+    include one shorter than Sq (its first rows see no key) and a ragged tail."""
+    Hkv = 2
+    lens = [333, 3, 1200, 40]
+    inp = fi.split_decode_inputs(70 + Sq, 4, G * Hkv, Hkv, 128, lens, page_size, Sq=Sq)
+    log(f"gqa decode multi Sq={Sq} G={G} page={page_size}")
+    o, lse = check(fa, inp, f"gqa multi Sq={Sq} G={G} page={page_size}")
+    if Sq > 3:
+        assert np.all(o[1, :Sq - 3] == 0) and np.all(np.isneginf(lse[1, :, :Sq - 3]))
+
+
+@pytest.mark.parametrize("splits", [1, 3, 0])
+def test_gqa_decode_multi_token_splits(fa, splits):
+    inp = fi.split_decode_inputs(77, 2, 16, 4, 128, [2000, 777], 16, Sq=4, dtype="fp16")
+    log(f"gqa decode multi splits={splits}")
+    check(fa, inp, f"gqa multi splits={splits}", num_splits=splits)
+
+
+# --------------------------------------------------------------------------
 # MLA decode, shared [ckv | kpe] pool
 # --------------------------------------------------------------------------
 
