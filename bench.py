@@ -129,6 +129,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--cpu-budget", type=float, default=12.0,
                     help="seconds of CPU oracle work for the baseline (0 = skip)")
+    ap.add_argument("--mla-page-sizes", action="store_true",
+                    help="also time the MLA decode workload with page sizes 16 and 64 "
+                         "(fresh pools and page tables of the same seeded recipe)")
     ap.add_argument("--no-mask", action="store_true",
                     help="skip the masked-prefill measurement (fa_prefill_mask)")
     ap.add_argument("--traffic", action="store_true",
@@ -210,6 +213,19 @@ def main():
                                                   16, inp5.max_seq_len, fa.FA_KV_SPLIT)
     ws5 = torch.empty(max(ws5_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
 
+    # Workload 4 decoding 2 new tokens per sequence at once (the same pool and table).
+    q4m = to_dev(fi.normal_bits((inp4.B, 2, inp4.Hq, 576), "bf16", fi.rng_for(4, fi.T_Q)))
+    o4m = torch.empty((inp4.B, 2, inp4.Hq, 512), dtype=torch.bfloat16, device=dev)
+    ws4m_bytes = fa.fa_decode_multi_workspace_size(inp4.B, 2, inp4.Hq, 1, 576, 512, 1,
+                                                   inp4.max_seq_len, fa.FA_KV_MLA_SHARED)
+    ws4m = torch.empty(max(ws4m_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
+
+    def decode_mla_multi_pass():
+        fa.fa_decode_paged_multi(q4m, pool4, pool4.shape[0], pt4, sl4, o4m, None, inp4.B, 2,
+                                 inp4.Hq, 1, 576, 512, 1, inp4.max_pages, inp4.max_seq_len,
+                                 fa.FA_KV_MLA_SHARED, inp4.scale, 0, fa.FA_BF16, ws4m,
+                                 ws4m_bytes, stream=sid)
+
     def decode_multi_pass():
         fa.fa_decode_paged_multi(q5, pool5, pool5.shape[0], pt5, sl5, o5, None, inp5.B, inp5.Sq,
                                  inp5.Hq, inp5.Hkv, 128, 128, 16, inp5.max_pages,
@@ -270,18 +286,22 @@ def main():
         torch.cuda.synchronize()
         t_pfm = sum(e0.elapsed_time(e1) for e0, e1 in ev_m) / 1e3
 
-    for _ in range(2):
-        decode_multi_pass()
-    ev_d5 = []
-    for _ in range(args.steps):
-        flush_sum = flush.sum()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        decode_multi_pass()
-        e1.record(stream)
-        ev_d5.append((e0, e1))
-    torch.cuda.synchronize()
-    t_d5 = sum(e0.elapsed_time(e1) for e0, e1 in ev_d5) / 1e3
+    def timed_cold(fn):
+        for _ in range(2):
+            fn()
+        evs = []
+        for _ in range(args.steps):
+            flush_sum = flush.sum()  # noqa: F841
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            evs.append((e0, e1))
+        torch.cuda.synchronize()
+        return sum(e0.elapsed_time(e1) for e0, e1 in evs) / 1e3
+
+    t_d5 = timed_cold(decode_multi_pass)
+    t_d4m = timed_cold(decode_mla_multi_pass)
 
     t_pf = sum(e[0].elapsed_time(e[1]) for e in events) / 1e3  # s
     t_dec = sum(e[2].elapsed_time(e[3]) for e in events) / 1e3
@@ -371,6 +391,47 @@ def main():
             "kernel": "fa_decode_paged_multi call (GQA decode kernel + split combine)",
         },
     }
+    bytes4m = decode_bytes(inp4) + inp4.B * inp4.Hq * (576 + 512) * 2  # a second q and o row
+    d4m_gbs = bytes4m * K / t_d4m / 1e9
+    result["decode_mla_multi"] = {
+        "metric": "paged MLA decode of 2 new tokens per sequence GB/s (%HBM peak)",
+        "value": round(d4m_gbs, 1),
+        "unit": "GB/s",
+        "us_per_call": round(t_d4m / K * 1e6, 2),
+        "bytes_per_call": bytes4m,
+        "workload": "MLA batch 128 x 64 heads x 2048 tokens, page 1, 2 new tokens each "
+                    "(causal among themselves), bf16; cold",
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(d4m_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(d4m_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "fa_decode_paged_multi call (MLA decode kernel, 64-row workgroups)",
+        },
+    }
+    if args.mla_page_sizes:
+        per_ps = {}
+        for ps in (1, 16, 64):
+            inp_ps = fi.mla_decode_inputs(4, 128, 64, 2048, page_size=ps)
+            q_ps, pool_ps = to_dev(inp_ps.q), to_dev(inp_ps.pool)
+            pt_ps = torch.from_numpy(inp_ps.page_table).to(dev)
+            sl_ps = torch.from_numpy(inp_ps.seq_lens).to(dev)
+            wsb_ps = fa.fa_decode_workspace_size(128, 64, 1, 576, 512, ps, 2048,
+                                                 fa.FA_KV_MLA_SHARED)
+            ws_ps = torch.empty(max(wsb_ps, 16) // 4 + 4, dtype=torch.float32, device=dev)
+
+            def ps_pass():
+                fa.fa_decode_paged(q_ps, pool_ps, pool_ps.shape[0], pt_ps, sl_ps, o4, None, 128,
+                                   64, 1, 576, 512, ps, inp_ps.max_pages, 2048,
+                                   fa.FA_KV_MLA_SHARED, inp_ps.scale, 0, fa.FA_BF16, ws_ps,
+                                   wsb_ps, stream=sid)
+            t_ps = timed_cold(ps_pass)
+            per_ps[str(ps)] = {"us_per_call": round(t_ps / K * 1e6, 2),
+                               "GB/s": round(decode_bytes(inp_ps) * K / t_ps / 1e9, 1)}
+            del q_ps, pool_ps, pt_ps, sl_ps, ws_ps
+        result["decode_mla_page_sizes"] = per_ps
     if t_pfm is not None:
         pfm_tflops = flops3 * K / t_pfm / 1e12
         result["prefill_mask"] = {

@@ -211,12 +211,13 @@ def with_mask(inp: PrefillInputs, c: int, kind: str, batched: bool = False,
 
 def mla_decode_inputs(c: int, B: int, Hq: int, seq_len: int, D_qk: int = 576, D_v: int = 512,
                       page_size: int = 1, dtype: str = BF16,
-                      scale: Optional[float] = None) -> DecodeInputs:
+                      scale: Optional[float] = None, Sq: int = 1) -> DecodeInputs:
     """Paged MLA decode: every sequence holds ``seq_len`` tokens; the pool has
-    exactly B * seq_len / page_size pages, assigned by one seeded permutation."""
+    exactly B * seq_len / page_size pages, assigned by one seeded permutation.
+    With Sq > 1 the queries are each sequence's last Sq tokens, q [B, Sq, Hq, D_qk]."""
     assert seq_len % page_size == 0
     n_pages = B * seq_len // page_size
-    q = normal_bits((B, Hq, D_qk), dtype, rng_for(c, T_Q))
+    q = normal_bits((B, Sq, Hq, D_qk) if Sq > 1 else (B, Hq, D_qk), dtype, rng_for(c, T_Q))
     pool = normal_bits((n_pages, page_size, D_qk), dtype, rng_for(c, T_POOL))
     perm = rng_for(c, T_PERM).permutation(n_pages).astype(np.int32)
     page_table = np.ascontiguousarray(perm.reshape(B, seq_len // page_size))
@@ -224,7 +225,7 @@ def mla_decode_inputs(c: int, B: int, Hq: int, seq_len: int, D_qk: int = 576, D_
     if scale is None:
         scale = 1.0 / math.sqrt(192.0)
     return DecodeInputs(q, pool, page_table, seq_lens, B, Hq, 1, D_qk, D_v, page_size,
-                        seq_len, "mla", f32(scale), dtype)
+                        seq_len, "mla", f32(scale), dtype, Sq)
 
 
 def split_decode_inputs(c: int, B: int, Hq: int, Hkv: int, D: int, lens, page_size: int,

@@ -254,7 +254,7 @@ def decode_paged(q, kv_pool, page_table, seq_lens, *, layout: int, scale: float,
                  num_splits: int = 0, out=None, return_lse: bool = False, workspace=None,
                  stream=None):
     """Paged decode on torch tensors. q [B, Hq, D_qk], or [B, Sq, Hq, D_qk] for
-    Sq new tokens per sequence (causal, bottom-right; split K/V layout only);
+    Sq new tokens per sequence (causal, bottom-right);
     kv_pool per layout; page_table [B, max_pages] int32; seq_lens [B] int32
     (device). o has q's leading shape; lse is [B, Hq] or [B, Hq, Sq]."""
     import torch
@@ -290,8 +290,12 @@ def _decode_multi(q, kv_pool, page_table, seq_lens, *, layout, scale, max_seq_le
                   D_v, num_splits, out, return_lse, workspace, stream):
     import torch
     B, Sq, Hq, D_qk = q.shape
-    Hkv = kv_pool.shape[2]
-    D_v = D_qk if D_v is None else D_v
+    if layout == FA_KV_MLA_SHARED:
+        Hkv = 1
+        D_v = 512 if D_v is None else D_v
+    else:
+        Hkv = kv_pool.shape[2]
+        D_v = D_qk if D_v is None else D_v
     if out is None:
         out = torch.empty((B, Sq, Hq, D_v), dtype=q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None

@@ -120,9 +120,9 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
     // 32-head workgroups, which need no split.
     int nh = env_int("FA_MLA_HEADS", 0);
     if (nh != 32 && nh != 64)
-      nh = Hq <= 32 || (!allow_split && max_seq_len > MLA_MAX_CHUNK) ? 32 : 64;
+      nh = Hq * Sq <= 32 || (!allow_split && max_seq_len > MLA_MAX_CHUNK) ? 32 : 64;
     pl.heads_per_wg = nh;
-    pl.n_hblk = ceil_div(Hq, nh);
+    pl.n_hblk = ceil_div(Hq * Sq, nh);  // rows: new tokens x heads
     units = (int64_t)B * pl.n_hblk;   // one workgroup per unit
     target = planner_cus();           // one 8-wave workgroup per CU
     if (nh == 64) min_splits = ceil_div(std::max(1, max_seq_len), MLA_MAX_CHUNK);
@@ -343,7 +343,6 @@ static int decode_impl(const void* q, const void* kv_pool, int num_pages,
                         page_size, max_pages_per_seq, max_seq_len, layout, dtype);
   if (rc != FA_OK) return rc;
   if (Sq < 1 || Sq > 64) return FA_ERR_SHAPE;
-  if (Sq > 1 && layout != FA_KV_SPLIT) return FA_ERR_UNSUPPORTED;
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
   if (B == 0) return FA_OK;
   const DecodePlan pl =
@@ -370,6 +369,7 @@ static int decode_impl(const void* q, const void* kv_pool, int num_pages,
     p.part_o = part_o;
     p.part_lse = part_lse;
     p.B = B;
+    p.Sq = Sq;
     p.Hq = Hq;
     p.page_size = page_size;
     p.max_pages = max_pages_per_seq;

@@ -38,6 +38,10 @@
 //    issued several MFMAs ahead of their use; the running max moves only when
 //    it grows by more than 2^8, so the 64 O accumulators per lane are rarely
 //    rescaled; row reductions use lane swaps (no LDS);
+//  * several new tokens per sequence (Sq > 1) share the workgroup's rows with
+//    the heads: row r is new token r % Sq of head r / Sq, so the tokens of a
+//    head sit side by side and every row of the workgroup uses each loaded
+//    K/V row; token i sees the cached tokens up to position seq_len - Sq + i;
 //  * tokens past the split's end are masked and rows without a valid token
 //    (or with a page id out of range) are zeroed in registers before they
 //    reach LDS (a NaN in an unused pool slot never reaches the output).
@@ -91,13 +95,18 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
   blk /= S;
   const int hb = blk % p.n_hblk;
   const int b = blk / p.n_hblk;
-  const int head = hb * NH + 16 * hg + c16;
+  const int rig = hb * NH + 16 * hg + c16;  // row: new token rig % Sq, head rig / Sq
+  const int qtok = rig % p.Sq;
+  const int head = rig / p.Sq;
   const bool hvalid = head < p.Hq;
 
   const int seq_len = min(max(p.seq_lens[b], 0), p.max_seq_len);
   const int t0 = split * p.chunk;
   const int n_tok = max(min(p.chunk, seq_len - t0), 0);
   const int n_steps = (n_tok + C::STEP_TOK - 1) / C::STEP_TOK;
+  // Last visible token of this row (split-local) and the smallest over the rows.
+  const int lim = min(n_tok - 1, seq_len - p.Sq + qtok - t0);
+  const int lim_lo = min(n_tok - 1, seq_len - p.Sq - t0);
 
   // Staging: lane l of wave w holds chunk 8 cb + ((l >> 3) ^ (rb & 1)) of
   // token row 8 rb + ((l & 7) ^ 4 ((l >> 4) & 1)) of a tile (the inverse of
@@ -147,7 +156,8 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
   for (int d = 0; d < INFL; ++d) pg[d] = pt_load(d);
   u32x4 qf[MLA_QS];
   {
-    const char* qrow = (const char*)p.q + ((int64_t)b * p.Hq + (hvalid ? head : 0)) * MLA_ROWB;
+    const char* qrow =
+        (const char*)p.q + (((int64_t)b * p.Sq + qtok) * p.Hq + (hvalid ? head : 0)) * MLA_ROWB;
 #pragma unroll
     for (int i = 0; i < MLA_QS; ++i) qf[i] = ldg16(qrow + (32 * (MLA_QS * kh + i) + 8 * gq) * 2);
   }
@@ -264,12 +274,12 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
 #pragma unroll
     for (int i = 0; i < VPD; ++i) vread(i);
     __builtin_amdgcn_sched_barrier(0);
-    if (tok0 + DEC_TILE > n_tok) {
+    if (tok0 + DEC_TILE - 1 > lim_lo) {  // past the split's end or a row's position
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          if (tok0 + 16 * (gq >> 1) + 8 * kb + 4 * (gq & 1) + i >= n_tok) sacc[kb][i] = -INFINITY;
+          if (tok0 + 16 * (gq >> 1) + 8 * kb + 4 * (gq & 1) + i > lim) sacc[kb][i] = -INFINITY;
     }
     float mx = fmaxf(fmaxf(fmaxf(sacc[0][0], sacc[0][1]), fmaxf(sacc[0][2], sacc[0][3])),
                      fmaxf(fmaxf(sacc[1][0], sacc[1][1]), fmaxf(sacc[1][2], sacc[1][3])));
@@ -360,10 +370,11 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
   if (!hvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
-  // The output row, or with several splits this split's partial row (same
-  // 16-bit type; the combine weighs the partials by their lse).
-  const int64_t row = (int64_t)b * p.Hq + head;
-  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Hq + row;
+  // The output row ([B, Sq, Hq] order), or with several splits this split's
+  // partial row (same 16-bit type; the combine weighs the partials by their
+  // lse and writes lse as [B, Hq, Sq]).
+  const int64_t row = ((int64_t)b * p.Sq + qtok) * p.Hq + head;
+  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Sq * p.Hq + row;
   char* orow = (char*)(S == 1 ? p.o : p.part_o) + (prow * MLA_DV + MLA_DVW * kh) * 2;
 #pragma unroll
   for (int db = 0; db < NPV; ++db) {
@@ -371,8 +382,12 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
                   T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
     *(u32x2*)(orow + (16 * db + 4 * gq) * 2) = v;
   }
-  float* lrow = S == 1 ? p.lse : p.part_lse;
-  if (lrow && gq == 0 && kh == 0) lrow[prow] = lse;
+  if (gq == 0 && kh == 0) {
+    if (S > 1)
+      p.part_lse[prow] = lse;
+    else if (p.lse)
+      p.lse[((int64_t)b * p.Hq + head) * p.Sq + qtok] = lse;
+  }
 }
 
 template <typename TI, int NH>

@@ -55,17 +55,17 @@ struct DecodeSplitParams {
 
 // Paged MLA decode, shared pool [P, page, 576]; K = row, V = row[0:512].
 struct DecodeMlaParams {
-  const void* q;  // [B, Hq, 576]
+  const void* q;  // [B, Sq, Hq, 576]
   const void* pool;
   const int32_t* page_table;
   const int32_t* seq_lens;
   void* o;  // [B, Hq, 512]
   float* lse;
-  void* part_o;     // [S, B, Hq, 512] in the input's 16-bit type when n_splits > 1
-  float* part_lse;  // [S, B, Hq]
-  int B, Hq, page_size, max_pages, num_pages, max_seq_len;
-  int heads_per_wg;  // query heads per workgroup: 64 or 32
-  int n_hblk;        // ceil(Hq / heads_per_wg)
+  void* part_o;     // [S, B, Sq, Hq, 512] in the input's 16-bit type when n_splits > 1
+  float* part_lse;  // [S, B, Sq, Hq]
+  int B, Sq, Hq, page_size, max_pages, num_pages, max_seq_len;
+  int heads_per_wg;  // query rows (new token x head) per workgroup: 64 or 32
+  int n_hblk;        // ceil(Hq * Sq / heads_per_wg)
   int chunk;         // tokens per split (multiple of 32; <= MLA_MAX_CHUNK with 64 heads)
   int n_splits;
   int q_neg;

@@ -173,9 +173,8 @@ int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
  * once per (sequence, K/V head).
  *   q   [B, Sq, Hq, D_qk]; o [B, Sq, Hq, D_v]; lse [B, Hq, Sq] fp32 or NULL
  *   Sq  1 .. 64
- * FA_KV_SPLIT layout only for Sq > 1 (FA_ERR_UNSUPPORTED otherwise). A row
- * whose position is negative (seq_lens[b] < Sq) sees no key: o = 0, lse =
- * -inf. Every other argument is as for fa_decode_paged; the workspace size
+ * Both pool layouts. A row whose position is negative (seq_lens[b] < Sq)
+ * sees no key: o = 0, lse = -inf. Every other argument is as for fa_decode_paged; the workspace size
  * comes from fa_decode_multi_workspace_size.
  */
 int fa_decode_paged_multi(const void* q, const void* kv_pool, int num_pages,

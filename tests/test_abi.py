@@ -75,7 +75,11 @@ def test_decode_multi_validation(fa):
 
     assert _err(call, Sq=0) == -2
     assert _err(call, Sq=65) == -2
-    assert _err(call, layout=fa.FA_KV_MLA_SHARED, Dqk=576, Dv=512, Hkv=1) == -3
+    # MLA: 128 sequences x 2 new tokens x 64 heads fill 256 64-row workgroups unsplit
+    mla = fa.FA_KV_MLA_SHARED
+    assert fa.fa_decode_multi_workspace_size(128, 2, 64, 1, 576, 512, 1, 2048, mla, 0) == 0
+    assert (fa.fa_decode_multi_workspace_size(128, 2, 64, 1, 576, 512, 1, 2048, mla, 2)
+            == 2 * 128 * 2 * 64 * (512 * 2 + 4))
     # rows = new tokens x heads: 4 sequences x 4 tokens x 32 heads of 16-bit partials + fp32 lse
     ws = fa.fa_decode_multi_workspace_size(4, 4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT, 3)
     assert ws == 3 * 4 * 4 * 32 * (128 * 2 + 4)

@@ -197,6 +197,21 @@ def test_mla_decode_long_without_workspace(fa):
     assert_lse(to_f64(lse), ref_lse, "mla long, no workspace")
 
 
+@pytest.mark.parametrize("heads", ["32", "64"])
+@pytest.mark.parametrize("Sq,Hq,splits", [(2, 64, 0), (3, 16, 1), (4, 128, 2), (2, 48, 3)])
+def test_mla_decode_multi_token(fa, heads, Sq, Hq, splits, monkeypatch):
+    """Several new tokens per sequence with the shared MLA pool: rows are
+    (token, head) pairs of the workgroup; lengths shorter than Sq included."""
+    monkeypatch.setenv("FA_MLA_HEADS", heads)
+    inp = _mla_ragged(80 + Sq, 3, Hq, 400, 1, [400, 2, 129])
+    inp.q = fi.normal_bits((3, Sq, Hq, 576), "bf16", fi.rng_for(80 + Sq, fi.T_Q))
+    inp.Sq = Sq
+    log(f"mla decode multi heads/wg={heads} Sq={Sq} Hq={Hq} splits={splits}")
+    o, lse = check(fa, inp, f"mla multi Sq={Sq} Hq={Hq}", num_splits=splits)
+    if Sq > 2:
+        assert np.all(o[1, :Sq - 2] == 0) and np.all(np.isneginf(lse[1, :, :Sq - 2]))
+
+
 def test_mla_decode_fp16_and_empty(fa):
     inp = _mla_ragged(53, 3, 64, 256, 1, [256, 0, 100], dtype="fp16")
     o, lse = check(fa, inp, "mla fp16")
