@@ -121,45 +121,57 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
   const int cp_dst = MLA_TILEB * cp_tile + 1024 * (9 * rb + cb0) + 16 * lane;
 
   const int32_t* ptab = p.page_table + (int64_t)b * p.max_pages;
+  // Page-table entries are read at keys clamped to max_seq_len - 1 (always
+  // inside the table, whose rows cover max_seq_len tokens), so these loads do
+  // not wait for the sequence length; entries past the split's tokens are
+  // ignored. The query loads follow them, so three round trips to memory
+  // (length, table, queries) overlap.
+  const int key_cap = max(p.max_seq_len - 1, 0);
+  constexpr int PER = C::ROWID_LDS ? MLA_MAX_CHUNK / MLA_THREADS : 1;
+  int page[PER];
   if constexpr (C::ROWID_LDS) {
-    // All of a thread's page-table loads are issued before any is used.
-    constexpr int PER = MLA_MAX_CHUNK / MLA_THREADS;
-    int page[PER];
 #pragma unroll
     for (int k = 0; k < PER; ++k) {
-      const int key = t0 + tid + MLA_THREADS * k;
-      page[k] = tid + MLA_THREADS * k < n_tok ? ptab[PS > 0 ? key / PS : key / p.page_size] : -1;
+      const int key = min(t0 + tid + MLA_THREADS * k, key_cap);
+      page[k] = ptab[PS > 0 ? key / PS : key / p.page_size];
     }
-#pragma unroll
-    for (int k = 0; k < PER; ++k) {
-      const int key = t0 + tid + MLA_THREADS * k;
-      const int slot = PS > 0 ? key % PS : key % p.page_size;
-      rowid[tid + MLA_THREADS * k] =
-          (unsigned)page[k] < (unsigned)p.num_pages ? page[k] * p.page_size + slot : -1;
-    }
-    __syncthreads();
   }
   // Pool row (ROWID_LDS) or page-table entry of this lane's row in step s (a
   // token past the split's end reads an entry that exists and is ignored).
   auto pt_load = [&](int s) -> int {
-    const int tok = min(s * C::STEP_TOK + cp_row, max(n_tok - 1, 0));
-    if constexpr (C::ROWID_LDS) return rowid[tok];
-    const int key = t0 + tok;
+    if constexpr (C::ROWID_LDS) return rowid[min(s * C::STEP_TOK + cp_row, max(n_tok - 1, 0))];
+    const int key = min(t0 + s * C::STEP_TOK + cp_row, key_cap);
     return ptab[PS > 0 ? key / PS : key / p.page_size];
   };
+  int pg[INFL];
+  if constexpr (!C::ROWID_LDS) {
+#pragma unroll
+    for (int d = 0; d < INFL; ++d) pg[d] = pt_load(d);
+  }
 
   // Query fragments (B operand, 32 dims per MFMA step) of this wave's half of
   // the dims: steps 9 kh .. 9 kh + 8. A wave without valid heads uses head 0's
   // (finite) query and stores nothing.
-  int pg[INFL];
-#pragma unroll
-  for (int d = 0; d < INFL; ++d) pg[d] = pt_load(d);
   u32x4 qf[MLA_QS];
   {
     const char* qrow =
         (const char*)p.q + (((int64_t)b * p.Sq + qtok) * p.Hq + (hvalid ? head : 0)) * MLA_ROWB;
 #pragma unroll
     for (int i = 0; i < MLA_QS; ++i) qf[i] = ldg16(qrow + (32 * (MLA_QS * kh + i) + 8 * gq) * 2);
+  }
+  if constexpr (C::ROWID_LDS) {
+#pragma unroll
+    for (int k = 0; k < PER; ++k) {
+      const int key = t0 + tid + MLA_THREADS * k;
+      const int slot = PS > 0 ? key % PS : key % p.page_size;
+      rowid[tid + MLA_THREADS * k] = tid + MLA_THREADS * k < n_tok &&
+                                             (unsigned)page[k] < (unsigned)p.num_pages
+                                         ? page[k] * p.page_size + slot
+                                         : -1;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int d = 0; d < INFL; ++d) pg[d] = pt_load(d);
   }
 
   const char* pool = (const char*)p.pool;

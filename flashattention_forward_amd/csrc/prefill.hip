@@ -352,7 +352,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 
   // Software pipeline (the scores of tile t+1 are computed on the matrix cores
   // while the softmax of tile t runs on the vector ALUs):
-  //   prologue: K(t0); wait; S(t0) = QK(t0); copy V(t0), K(t0+1)
+  //   prologue: copy K(t0), V(t0), K(t0+1); wait; S(t0) = QK(t0)
   //   step t:   wait for K(t+1), V(t); copy K(t+2), V(t+1);
   //             S(t+1) = QK(t+1); softmax(S(t)); O += P V(t)
   // One barrier per step also guarantees that the stages being refilled
@@ -363,14 +363,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   f32x16 sA[2], sB[2];
   float mx_pend = -INFINITY;
   if (t_begin < t_end) {
+    // All first copies (K(t0), V(t0), K(t0+1)) go out together with the query
+    // loads: the prologue waits for memory once, and the first step's wait
+    // finds them done.
     if constexpr (AMASK) load_mask(t_begin);
     issue_k(t_begin);
+    issue_v(t_begin);
+    if (t_begin + 1 < t_end) issue_k(t_begin + 1);
     wait_vmcnt<0>();
     lds_barrier();
     qk(sA, smem + k_stage(t_begin));
     mx_pend = tile_max(sA);
-    issue_v(t_begin);
-    if (t_begin + 1 < t_end) issue_k(t_begin + 1);
   }
   auto step = [&](auto mask_tag, int t, f32x16 (&cur)[2], f32x16 (&nxt)[2]) {
     constexpr bool MASK = decltype(mask_tag)::value;
