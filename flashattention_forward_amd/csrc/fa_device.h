@@ -93,15 +93,6 @@ template <> struct out_size<out_f16> { static constexpr int bytes = 2; };
 
 __device__ __forceinline__ u32x4 ldg16(const void* p) { return *(const u32x4*)p; }
 
-// Select the 16-bit halves of two dwords: lo16(a) | lo16(b) << 16 and
-// hi16(a) | hi16(b) << 16 (v_perm_b32 byte selects).
-__device__ __forceinline__ uint32_t pack_lo(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x05040100u);
-}
-__device__ __forceinline__ uint32_t pack_hi(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_perm(b, a, 0x07060302u);
-}
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // ds_read_b64_tr_b16: within each group of 16 lanes, lane j passes the address
@@ -154,28 +145,14 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) char*)p;
 }
 
-// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
-// lane l's 16 bytes from gsrc land at LDS address lds_base + 16 * l; lds_base
-// is wave-uniform and goes through M0, which is restored afterwards. (The
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4)
+// from a wave-uniform 64-bit base (SGPRs) plus a per-lane 32-bit byte offset:
+// lane l's 16 bytes land at LDS address lds_base + 16 * l; lds_base is
+// wave-uniform and goes through M0, which is restored afterwards. (The
 // instruction's immediate offset is left at 0: it would move the LDS side too.)
 // Issued from inline assembly so the compiler does not add a full vmcnt(0)
 // wait before every later LDS read; callers wait with wait_vmcnt<N>(), which
 // counts these copies like any vector load (they retire in issue order).
-__device__ __forceinline__ void dma16(const void* gsrc, uint32_t lds_base) {
-  uint32_t saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\t"
-      "s_mov_b32 m0, %2\n\t"
-      "s_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\t"
-      "s_mov_b32 m0, %0"
-      : "=&s"(saved)
-      : "v"(gsrc), "s"(__builtin_amdgcn_readfirstlane(lds_base))
-      : "memory");
-}
-
-// Same copy with a wave-uniform 64-bit base (SGPRs) and a per-lane 32-bit
-// byte offset: no per-lane 64-bit address arithmetic at all.
 __device__ __forceinline__ void dma16s(const void* sbase, uint32_t voff, uint32_t lds_base) {
   uint32_t saved;
   asm volatile(
@@ -220,24 +197,6 @@ __device__ __forceinline__ float sum_xor32(float v) {
 // applied as |scale| on -Q so the running max stays a max).
 __device__ __forceinline__ u32x4 neg16x8(u32x4 v) {
   return v ^ u32x4{0x80008000u, 0x80008000u, 0x80008000u, 0x80008000u};
-}
-
-// acc *= s for an MFMA accumulator that lives in AGPRs. Written as inline
-// assembly (read to a VGPR, multiply, write back) so that a rarely taken rescale
-// does not make the compiler keep the accumulators in VGPRs and copy them
-// around every MFMA.
-__device__ __forceinline__ void acc_scale(f32x4& acc, float s) {
-  float a0 = acc[0], a1 = acc[1], a2 = acc[2], a3 = acc[3];
-  float t;
-  asm volatile(
-      "v_accvgpr_read_b32 %4, %0\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %0, %4\n\t"
-      "v_accvgpr_read_b32 %4, %1\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %1, %4\n\t"
-      "v_accvgpr_read_b32 %4, %2\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %2, %4\n\t"
-      "v_accvgpr_read_b32 %4, %3\n\tv_mul_f32 %4, %4, %5\n\tv_accvgpr_write_b32 %3, %4\n\t"
-      "s_nop 2"
-      : "+a"(a0), "+a"(a1), "+a"(a2), "+a"(a3), "=&v"(t)
-      : "v"(s));
-  acc = f32x4{a0, a1, a2, a3};
 }
 
 // LDS tile layout shared by the direct-to-LDS copies: a tile of 16-byte chunks
