@@ -333,6 +333,13 @@ int fa_decode_num_splits(int B, int Hq, int Hkv, int D_qk, int D_v, int page_siz
   return plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, true).n_splits;
 }
 
+// Exponent scale |scale| log2(e). Zero is passed as the smallest positive
+// value, as for prefill: a masked score (-inf) must still give probability 0,
+// and exp2(s * 1e-30) == 1 in fp32 for every finite score.
+static float decode_exp_scale(float abs_scale) {
+  return std::max(abs_scale * 1.4426950408889634f, 1e-30f);
+}
+
 static int decode_impl(const void* q, const void* kv_pool, int num_pages,
                        const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
                        int B, int Sq, int Hq, int Hkv, int D_qk, int D_v, int page_size,
@@ -381,7 +388,7 @@ static int decode_impl(const void* q, const void* kv_pool, int num_pages,
     p.n_splits = pl.n_splits;
     p.q_neg = scale < 0.f;
     p.scale = std::fabs(scale);
-    p.scale_log2 = p.scale * 1.4426950408889634f;
+    p.scale_log2 = decode_exp_scale(p.scale);
     if ((int64_t)B * p.n_hblk * p.n_splits > kMaxGrid) return FA_ERR_SHAPE;
     e = launch_decode_mla(p, it, stream);
   } else {
@@ -410,7 +417,7 @@ static int decode_impl(const void* q, const void* kv_pool, int num_pages,
     p.n_units = (int)units;
     p.q_neg = scale < 0.f;
     p.scale = std::fabs(scale);
-    p.scale_log2 = p.scale * 1.4426950408889634f;
+    p.scale_log2 = decode_exp_scale(p.scale);
     e = launch_decode_split(p, it, stream);
   }
   if (e != hipSuccess) return FA_ERR_HIP;

@@ -3,6 +3,8 @@ against the CPU oracle, through the C ABI. Covers ragged and empty sequences,
 page sizes 1 / 16 / odd, NaN-poisoned unused slots, every split count, and the
 two full-size workloads (MLA batch 128 x 2048 tokens; GQA batch 4 with lengths
 U[1024, 32768]) in the bench's launch configuration."""
+import dataclasses
+
 import numpy as np
 import pytest
 
@@ -63,6 +65,23 @@ def test_gqa_decode_split_sweep(fa, splits):
     inp = fi.split_decode_inputs(40, 3, 8, 2, 128, [1500, 700, 64], 16)
     log(f"gqa decode splits={splits}")
     check(fa, inp, f"gqa splits={splits}", num_splits=splits)
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_gqa_decode_scale_zero(fa, splits):
+    """scale 0: every visible token has the same weight, and masked slots (past
+    a split's end) must still weigh 0, not NaN."""
+    inp = dataclasses.replace(fi.split_decode_inputs(44, 3, 8, 2, 128, [1500, 700, 64], 16),
+                              scale=0.0)
+    log(f"gqa decode scale 0 splits={splits}")
+    check(fa, inp, f"gqa scale 0 splits={splits}", num_splits=splits)
+
+
+@pytest.mark.parametrize("Sq", [1, 2])
+def test_mla_decode_scale_zero(fa, Sq):
+    inp = dataclasses.replace(fi.mla_decode_inputs(45, 3, 16, 1000, Sq=Sq), scale=0.0)
+    log(f"mla decode scale 0 Sq={Sq}")
+    check(fa, inp, f"mla scale 0 Sq={Sq}")
 
 
 def test_gqa_decode_fp16(fa):
