@@ -59,6 +59,12 @@ template <int D, int NW_> struct PfCfg {
   static constexpr int NCB = NCH / 8;         // 8-chunk blocks per key row
   static constexpr int TILE = PF_BN * D * 2;  // bytes of one K (or V) tile
   static constexpr int LDS = 4 * TILE;        // 2 K stages + 2 V stages
+  // LDS reserved per workgroup. Head size 64 with 4 waves needs only 32 KB
+  // and 164 VGPRs, so three workgroups would share a CU; the schedule is built
+  // for two waves per SIMD, and a third made the 1024-workgroup grid of the
+  // 4 x 16 x 2048 x 64 MHA run as 1 1/3 rounds (102.8 us against 93.2 us with
+  // 56 KB reserved, which leaves room for two).
+  static constexpr int LDS_RESERVE = (D == 64 && NW_ == 4) ? 56 * 1024 : LDS;
   static constexpr int NW = NW_;              // waves per workgroup
   static constexpr int BM = 32 * NW;          // query rows per workgroup
   static constexpr int BPW = 8 * NCB / NW;    // 1 KB blocks of a tile each wave copies
@@ -68,7 +74,7 @@ template <int D, int NW, typename TI, typename TO, bool CAUSAL, bool AMASK>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   using C = PfCfg<D, NW>;
   using T = in_traits<TI>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS];
+  __shared__ __attribute__((aligned(16))) char smem[C::LDS_RESERVE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
