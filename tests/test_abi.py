@@ -170,9 +170,12 @@ def test_decode_split_planning(fa, monkeypatch):
     assert fa.fa_decode_num_splits(64, 128, 1, 576, 512, 1, 2048, mla) == 1
     assert fa.fa_decode_workspace_size(64, 128, 1, 576, 512, 1, 2048, mla, 0) == 0
     monkeypatch.delenv("FA_MLA_HEADS")
-    # GQA, 4 sequences x 8 K/V heads: many splits over 32768 tokens
-    s = fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT)
-    assert 16 <= s <= 128
+    # GQA, 4 sequences x 8 K/V heads: four waves per SIMD over 32 units wants 128
+    # splits, capped at chunks of 8 tiles (256 tokens), rounded down to whole tiles
+    assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT) == 128
+    assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 23450, fa.FA_KV_SPLIT) == 92
+    # many sequences: few splits (4096 tokens, 32 x 8 units wants 16)
+    assert fa.fa_decode_num_splits(32, 32, 8, 128, 128, 16, 4096, fa.FA_KV_SPLIT) == 16
     # explicit request is honoured (clamped to the 32-token tiles available)
     assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 32768, fa.FA_KV_SPLIT, 3) == 3
     assert fa.fa_decode_num_splits(4, 32, 8, 128, 128, 16, 40, fa.FA_KV_SPLIT, 8) == 2
