@@ -116,26 +116,30 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
     return ok ? (int64_t)pg[r] * page_stride + (int64_t)slot * D * 2 : 0;
   };
 
-  u32x4 kcur[2][D / 32], knext[2][D / 32], vnext[8];
-  bool kok_cur[2], kok_next[2], vok[8];
-  auto load_tile = [&](const int (&pg)[10], int tt, u32x4 (&kr)[2][D / 32], bool (&kok)[2]) {
+  // One tile in flight: K of tile t + 1 is loaded into the registers that K
+  // of tile t has just fed to the score MFMAs, and V of tile t + 1 into the
+  // staging registers once V of tile t is in LDS.
+  u32x4 kr[2][D / 32], vr[8];
+  bool kok[2], vok[8];
+  auto load_k = [&](const int (&pg)[10], int tt) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
       const int64_t o = row_off(pg, kb, tt, kok[kb]);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) kr[kb][s] = ldg16(pool_g + o + (32 * s + 8 * gq) * 2);
     }
+  };
+  auto load_v = [&](const int (&pg)[10], int tt) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
       const int64_t o = row_off(pg, 2 + r, tt, vok[r]);
-      vnext[r] = ldg16(pool_g + o + kv_stride + c16 * 16);
+      vr[r] = ldg16(pool_g + o + kv_stride + c16 * 16);
     }
   };
   auto store_v = [&]() {
 #pragma unroll
     for (int r = 0; r < 8; ++r)
-      *(u32x4*)(vlds + ((gq + 4 * r) * DS_VS + c16 * 8) * 2) =
-          vok[r] ? vnext[r] : u32x4{0, 0, 0, 0};
+      *(u32x4*)(vlds + ((gq + 4 * r) * DS_VS + c16 * 8) * 2) = vok[r] ? vr[r] : u32x4{0, 0, 0, 0};
   };
 
   f32x4 oacc[D / 16];
@@ -144,32 +148,33 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = p.scale_log2;
 
-  int pg_a[10], pg_b[10];
+  // pg holds the page ids of the tile whose loads are issued next.
+  int pg[10];
   if (t0 < t1) {
-    fetch_pages(pg_a, t0);
-    fetch_pages(pg_b, t0 + DEC_TILE);
-    load_tile(pg_a, t0, kcur, kok_cur);
-    store_v();
-    wave_lds_sync();
+    fetch_pages(pg, t0);
+    load_k(pg, t0);
+    load_v(pg, t0);
+    fetch_pages(pg, t0 + DEC_TILE);
   }
   for (int tt = t0; tt < t1; tt += DEC_TILE) {
     const bool more = tt + DEC_TILE < t1;
-    if (more) {
-      // pg_b holds tile tt+32's pages; fetch tile tt+64's into pg_a.
-      load_tile(pg_b, tt + DEC_TILE, knext, kok_next);
-#pragma unroll
-      for (int r = 0; r < 10; ++r) pg_a[r] = pg_b[r];
-      fetch_pages(pg_b, tt + 2 * DEC_TILE);
-    }
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) {
-        const u32x4 kv = kok_cur[kb] ? kcur[kb][s] : u32x4{0, 0, 0, 0};
+        const u32x4 kv = kok[kb] ? kr[kb][s] : u32x4{0, 0, 0, 0};
         sacc[kb] = T::mma16(kv, qf[s], sacc[kb]);
       }
     }
+    if (more) load_k(pg, tt + DEC_TILE);
+    wave_lds_sync();  // the previous tile's V reads are done
+    store_v();
+    if (more) {
+      load_v(pg, tt + DEC_TILE);
+      fetch_pages(pg, tt + 2 * DEC_TILE);
+    }
+    wave_lds_sync();
     const bool tail = tt + DEC_TILE > t1;
     if (tail) {
 #pragma unroll
@@ -218,17 +223,6 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
       const u32x2 r0 = lds_read_tr16(va + 16 * db * 2);
       const u32x2 r1 = lds_read_tr16(va + (16 * DS_VS + 16 * db) * 2);
       oacc[db] = T::mma16(u32x4{r0[0], r0[1], r1[0], r1[1]}, pb, oacc[db]);
-    }
-    if (more) {
-      wave_lds_sync();
-      store_v();
-      wave_lds_sync();
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        kok_cur[kb] = kok_next[kb];
-#pragma unroll
-        for (int s = 0; s < D / 32; ++s) kcur[kb][s] = knext[kb][s];
-      }
     }
   }
 
