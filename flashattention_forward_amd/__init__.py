@@ -217,8 +217,8 @@ def prefill(q, k, v, *, causal: bool, scale: Optional[float] = None, out=None, o
             return_lse: bool = False, allow_split: bool = True, mask=None, stream=None):
     """Attention prefill on torch tensors q [B, Sq, Hq, D], k/v [B, Skv, Hkv, D]
     (bf16 or fp16, contiguous, on the GPU). ``mask`` is None or an additive mask
-    of q's dtype, [Sq, W] or [B, Sq, W] with W >= Skv rounded up to 4 and a
-    multiple of 4 (contiguous). Returns o [B, Sq, Hq, D] (and lse [B, Hq, Sq]
+    of q's dtype, [Sq, W] or [B, Sq, W] with W >= Skv rounded up to 8 and a
+    multiple of 8 (contiguous, 16-byte aligned). Returns o [B, Sq, Hq, D] (and lse [B, Hq, Sq]
     fp32 if asked)."""
     import torch
     B, Sq, Hq, D = q.shape

@@ -284,10 +284,14 @@ int fa_prefill_mask(const void* q, const void* k, const void* v, const void* mas
                     fa_dtype in_dtype, fa_dtype out_dtype, void* workspace,
                     size_t workspace_bytes, hipStream_t stream) {
   if (!mask) return FA_ERR_NULL;
-  if ((reinterpret_cast<uintptr_t>(mask) & 7u) != 0 || mask_stride % 4 != 0 ||
-      mask_batch_stride % 4 != 0)
+  // The kernel copies the mask in 16-byte pieces (8 keys), with per-row byte
+  // offsets of 32 bits.
+  if ((reinterpret_cast<uintptr_t>(mask) & 15u) != 0 || mask_stride % 8 != 0 ||
+      mask_batch_stride % 8 != 0)
     return FA_ERR_ALIGN;
-  if (mask_stride < ((int64_t)Skv + 3) / 4 * 4 || mask_batch_stride < 0) return FA_ERR_SHAPE;
+  if (mask_stride < ((int64_t)Skv + 7) / 8 * 8 || mask_batch_stride < 0 ||
+      (int64_t)Sq * mask_stride > (int64_t)1 << 30)
+    return FA_ERR_SHAPE;
   return prefill_impl(q, k, v, mask, mask_stride, mask_batch_stride, o, lse, B, Hq, Hkv, Sq,
                       Skv, D, causal, scale, in_dtype, out_dtype, workspace, workspace_bytes,
                       stream);

@@ -42,11 +42,13 @@
 //  * a workgroup may process one of several key splits; it then writes its
 //    normalised partial O and log-sum-exp for a separate combine kernel;
 //  * with an explicit additive mask (the KQ mask that the same llama.cpp page
-//    counts as memory traffic) every lane loads the 16 mask values of its
-//    query row for each 32-key block one tile ahead (8-byte loads from L2,
-//    into registers) and the scores are taken to the exponent's base-2 domain
-//    as fma(s, scale log2 e, mask log2 e) before the row max, so the running
-//    max, rescale and exponent work unchanged with a unit exponent scale.
+//    counts as memory traffic) each wave copies the mask of its 32 query rows
+//    for the next tile into its own LDS buffer with the same direct copies as
+//    K and V (8 rows x 128 bytes per instruction); every lane then reads the
+//    16 values of its row per 32-key block from LDS, and the scores are taken
+//    to the exponent's base-2 domain as fma(s, scale log2 e, mask log2 e)
+//    before the row max, so the running max, rescale and exponent work
+//    unchanged with a unit exponent scale.
 #include <type_traits>
 
 #include "fa_device.h"
@@ -68,13 +70,18 @@ template <int D, int NW_> struct PfCfg {
   static constexpr int NW = NW_;              // waves per workgroup
   static constexpr int BM = 32 * NW;          // query rows per workgroup
   static constexpr int BPW = 8 * NCB / NW;    // 1 KB blocks of a tile each wave copies
+  // With an additive mask each wave also holds one 4 KB mask tile (32 rows x
+  // 64 keys) after the K/V stages; 4 waves of head size 128 then take 80 KB,
+  // so two workgroups still share a CU.
+  static constexpr int MASK_LDS = NW * 4096;
+  static constexpr int LDS_MASKED = LDS + MASK_LDS > LDS_RESERVE ? LDS + MASK_LDS : LDS_RESERVE;
 };
 
 template <int D, int NW, typename TI, typename TO, bool CAUSAL, bool AMASK>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   using C = PfCfg<D, NW>;
   using T = in_traits<TI>;
-  __shared__ __attribute__((aligned(16))) char smem[C::LDS_RESERVE];
+  __shared__ __attribute__((aligned(16))) char smem[AMASK ? C::LDS_MASKED : C::LDS_RESERVE];
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -172,21 +179,51 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   const float sl2 = AMASK ? 1.f : p.scale_log2;
   const int q_last_wave = min(qw0 + 31, p.Sq - 1);
 
-  // Mask values of this lane's query row (rows past the end read the last
-  // row): chunk m of a tile holds keys k0 + 8 m + 4 h .. + 3, i.e. the four
-  // scores 4 (m & 3) .. + 3 of score block m >> 2. A chunk at or past the end
-  // of the keys reads chunk 0 instead (those keys are masked anyway).
+  // Mask tile of this wave in LDS: 4 blocks of 1 KB, block RB holding query
+  // rows 8 RB .. 8 RB + 7 of the wave and all 8 chunks (8 keys each) of the
+  // tile; row r, chunk k sits in 16-byte slot 8 (k ^ (RB & 1)) + r, so that
+  // one copy instruction moves 8 rows x 128 contiguous bytes and a read of
+  // one chunk by the wave's 32 rows spreads over the banks. Rows past the end
+  // of the queries copy the last row; in the last tile a chunk at or past the
+  // end of the keys copies chunk 0 instead (those keys are masked anyway, and
+  // the rest of the chunk holding the end lies inside the mask's row stride).
+  // Lane (c, h) needs keys 8 m + 4 h .. + 3 of chunk m, i.e. the four scores
+  // 4 (m & 3) .. + 3 of score block m >> 2.
   u32x2 mk[8];
-  const char* mrow = nullptr;
-  if constexpr (AMASK)
-    mrow = (const char*)p.mask +
-           ((int64_t)b * p.mask_bstride + (int64_t)min(qi, p.Sq - 1) * p.mask_stride) * 2;
-  auto load_mask = [&](int t) {
+  const char* mbase = nullptr;
+  uint32_t moff[4] = {};
+  int mchunk[4] = {};
+  const uint32_t mlds = smem_lds + C::LDS + 4096 * w;
+  const char* mread = smem + C::LDS + 4096 * w + 1024 * (c >> 3) + 16 * (c & 7) + 8 * h;
+  const int mflip = ((c >> 3) & 1) ? 128 : 0;
+  if constexpr (AMASK) {
+    mbase = (const char*)p.mask + (int64_t)b * p.mask_bstride * 2;
 #pragma unroll
-    for (int m = 0; m < 8; ++m) {
-      const int kk = t * PF_BN + 8 * m + 4 * h;
-      mk[m] = *(const u32x2*)(mrow + (kk < p.Skv ? kk : 0) * 2);
+    for (int i = 0; i < 4; ++i) {
+      const int row = min(qw0 + 8 * i + (lane & 7), p.Sq - 1);
+      mchunk[i] = (lane >> 3) ^ (i & 1);
+      moff[i] = (uint32_t)row * (uint32_t)(p.mask_stride * 2) + 16 * mchunk[i];
     }
+  }
+  auto issue_mask = [&](int t) {
+    const int k0 = t * PF_BN;
+    const char* src = mbase + (int64_t)k0 * 2;
+    if (k0 + PF_BN <= p.Skv) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) dma16s(src, moff[i], mlds + 1024 * i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        dma16s(src, k0 + 8 * mchunk[i] < p.Skv ? moff[i] : moff[i] - 16 * mchunk[i],
+               mlds + 1024 * i);
+    }
+  };
+  // Chunk m is at slot 8 (m ^ (RB & 1)) + r: 128 m, moved by -128 or +128 for
+  // odd row blocks.
+  auto read_mask = [&]() {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+      mk[m] = *(const u32x2*)(mread + 128 * m + ((m & 1) ? -mflip : mflip));
   };
   // Scores of the tile into the exponent domain: s * scale log2 e + mask log2 e.
   auto add_mask = [&](f32x16 (&sacc)[2]) {
@@ -372,7 +409,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     // All first copies (K(t0), V(t0), K(t0+1)) go out together with the query
     // loads: the prologue waits for memory once, and the first step's wait
     // finds them done.
-    if constexpr (AMASK) load_mask(t_begin);
+    if constexpr (AMASK) issue_mask(t_begin);
     issue_k(t_begin);
     issue_v(t_begin);
     if (t_begin + 1 < t_end) issue_k(t_begin + 1);
@@ -385,13 +422,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     constexpr bool MASK = decltype(mask_tag)::value;
     wait_vmcnt<0>();
     lds_barrier();
-    // (The mask values are used before any copy is issued: the compiler's own
-    // wait for them counts no inline-assembly copies and would be a full wait.)
-    if constexpr (AMASK) add_mask(cur);
+    if constexpr (AMASK) read_mask();
     if (t + 2 < t_end) issue_k(t + 2);
     if (t + 1 < t_end) issue_v(t + 1);
-    if constexpr (AMASK)
-      if (t + 1 < t_end) load_mask(t + 1);
+    if constexpr (AMASK) {
+      // The wave's mask buffer is refilled only once its reads have returned.
+      wave_lds_sync();
+      if (t + 1 < t_end) issue_mask(t + 1);
+      add_mask(cur);
+    }
     // After the last tile the block still computes scores from a stale K stage
     // (in bounds, never used): that keeps the block free of branches.
     // A tile wholly above this wave's causal diagonal is masked out entirely

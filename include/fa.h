@@ -109,14 +109,15 @@ int fa_prefill_ex(const void* q, const void* k, const void* v, void* o, float* l
  *                      hides the key; a row whose keys are all hidden gives
  *                      o = 0 and lse = -inf). mask_batch_stride 0 shares one
  *                      [Sq, Skv] mask over the batch.
- *   mask_stride        elements between rows: a multiple of 4 and at least Skv
- *                      rounded up to 4 (the kernel reads keys in groups of 4;
- *                      entries past Skv are read but never used)
- *   mask_batch_stride  0, or elements between batch entries (a multiple of 4)
- * The mask pointer must be 8-byte aligned (FA_ERR_ALIGN otherwise); a null mask
- * is FA_ERR_NULL. Every other argument is as for fa_prefill_ex. The mask is read
- * from device memory by every query head (it is small against K and V and
- * stays in L2).
+ *   mask_stride        elements between rows: a multiple of 8 and at least Skv
+ *                      rounded up to 8 (the kernel copies keys in groups of 8;
+ *                      entries past Skv are read but never used); Sq *
+ *                      mask_stride at most 2^30 (FA_ERR_SHAPE otherwise)
+ *   mask_batch_stride  0, or elements between batch entries (a multiple of 8)
+ * The mask pointer must be 16-byte aligned (FA_ERR_ALIGN otherwise, also for a
+ * stride that is not a multiple of 8); a null mask is FA_ERR_NULL. Every other
+ * argument is as for fa_prefill_ex. The mask is read from device memory by
+ * every query head (it is small against K and V and stays in L2).
  */
 int fa_prefill_mask(const void* q, const void* k, const void* v, const void* mask,
                     int64_t mask_stride, int64_t mask_batch_stride, void* o, float* lse, int B,

@@ -60,11 +60,12 @@ def test_prefill_mask_validation(fa):
                                   0.1, fa.FA_BF16, fa.FA_BF16, None, 0, stream=0)
 
     assert _err(call, mask=None) == -1
-    assert _err(call, mask=A + 4) == -4  # mask rows are read 8 bytes at a time
-    assert _err(call, stride=18) == -4
-    assert _err(call, bstride=6) == -4
-    assert _err(call, stride=12) == -2  # Skv = 13 needs rows of >= 16 elements
-    assert _err(call, bstride=-4) == -2
+    assert _err(call, mask=A + 8) == -4  # mask rows are copied 16 bytes at a time
+    assert _err(call, stride=20) == -4
+    assert _err(call, bstride=12) == -4
+    assert _err(call, stride=8) == -2  # Skv = 13 needs rows of >= 16 elements
+    assert _err(call, bstride=-8) == -2
+    assert _err(call, stride=1 << 28) == -2  # Sq (8) x stride > 2^30: 32-bit row offsets
 
 
 def test_decode_multi_validation(fa):

@@ -214,7 +214,7 @@ def test_gqa_ubatch_full_size_sampled(fa):
 
 def run_masked(fa, inp, *, stride_pad=0):
     """Runs fa.prefill with inp.mask (bits [Bm, Sq, W]); W is the mask's own
-    row stride (Skv rounded up to 4 plus padding, NaN-poisoned past Skv)."""
+    row stride (Skv rounded up to 8 plus padding, NaN-poisoned past Skv)."""
     import torch
     q, k, v = (to_dev(x, inp.in_dtype) for x in (inp.q, inp.k, inp.v))
     m = to_dev(inp.mask, inp.in_dtype)
@@ -229,7 +229,7 @@ def run_masked(fa, inp, *, stride_pad=0):
 def _mask_inputs(c, shape, kind, batched=False, pad=0):
     B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
     inp = fi.prefill_inputs(c, B, Hq, Hkv, Sq, Skv, D, causal, it, ot)
-    stride = (Skv + 3) // 4 * 4 + pad
+    stride = (Skv + 7) // 8 * 8 + pad
     return fi.with_mask(inp, c, kind, batched=batched, stride=stride)
 
 
@@ -249,7 +249,7 @@ def test_prefill_mask_parity(fa, shape, kind):
     """softmax(scale Q K^T + M) V for random, packed-sequence, distance-bias and
     hidden-row masks (one shared [Sq, W] matrix, W padded with NaN past Skv)."""
     log(f"prefill mask {kind} {shape}")
-    inp = _mask_inputs(60, shape, kind, pad=4)
+    inp = _mask_inputs(60, shape, kind, pad=8)
     o, lse = run_masked(fa, inp)
     ref, ref_lse = oracle.prefill(inp)
     assert_parity(to_f64(o), ref, shape[7], f"mask {kind} {shape}")
@@ -296,7 +296,7 @@ def test_prefill_zero_mask_equals_unmasked(fa):
     shape = (1, 8, 2, 300, 700, 128, True, "bf16", "bf16")
     inp = fi.prefill_inputs(63, *shape)
     q, k, v = (to_dev(x, "bf16") for x in (inp.q, inp.k, inp.v))
-    zero = torch.zeros((300, 700), dtype=torch.bfloat16, device=q.device)
+    zero = torch.zeros((300, 704), dtype=torch.bfloat16, device=q.device)  # rows of 8k
     o0 = fa.prefill(q, k, v, causal=True, scale=inp.scale)
     o1 = fa.prefill(q, k, v, causal=True, scale=inp.scale, mask=zero)
     torch.cuda.synchronize()
