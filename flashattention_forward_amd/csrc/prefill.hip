@@ -460,31 +460,61 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
 
   // Epilogue: both lane halves hold parts of the row sum.
   const float l_tot = sum_xor32(l_run);
-  if (!q_ok) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // (With a mask m_run is in the base-2 domain.)
   const float lse = l_tot > 0.f ? (AMASK ? m_run * 0.6931471805599453f : m_run * p.scale) +
                                       __logf(l_tot)
                                 : -INFINITY;
-  // The output row, or with several splits this split's partial row (in the
-  // output's type; the combine weighs the partials by their lse).
-  const int64_t row = ((int64_t)b * p.Sq + qi) * p.Hq + hq;
-  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Sq * p.Hq + row;
-  char* orow = (char*)(S == 1 ? p.o : p.part_o) + prow * D * out_size<TO>::bytes;
+  // The output rows, or with several splits this split's partial rows (in the
+  // output's type; the combine weighs the partials by their lse). Query row i
+  // of head hq is row (b * Sq + i) * Hq + hq of the output.
+  constexpr int OB = out_size<TO>::bytes;
+  char* obase = (char*)(S == 1 ? p.o : p.part_o) +
+                (S == 1 ? 0 : (int64_t)split * p.B * p.Sq * p.Hq * D * OB);
+  auto out_row = [&](int i) { return obase + (((int64_t)b * p.Sq + i) * p.Hq + hq) * D * OB; };
+  // A 16-bit output goes through LDS: each lane holds 4 columns of one row per
+  // store, so direct stores would touch the 32 rows of the wave (32 cache
+  // lines) per instruction. Instead every wave writes its 32 rows into its own
+  // slice of the (now idle) K/V stages, 16-byte chunk q of row r at chunk
+  // q ^ (r % NCO), and stores them back a few whole rows per instruction.
+  constexpr int RB = D * 2;     // bytes per row
+  constexpr int NCO = RB / 16;  // 16-byte chunks per row
+  constexpr bool LDS_EPI = OB == 2 && NW * 32 * RB <= C::LDS;
+  if constexpr (LDS_EPI) {
+    lds_barrier();  // every wave has finished reading the K/V stages
+    char* ot = smem + w * 32 * RB;
 #pragma unroll
-  for (int db = 0; db < D / 32; ++db)
+    for (int db = 0; db < D / 32; ++db)
 #pragma unroll
-    for (int i4 = 0; i4 < 4; ++i4) {
-      const int d = 32 * db + 8 * i4 + 4 * h;
-      store4(TO{}, orow + d * out_size<TO>::bytes, oacc[db][4 * i4] * inv,
-             oacc[db][4 * i4 + 1] * inv, oacc[db][4 * i4 + 2] * inv,
-             oacc[db][4 * i4 + 3] * inv);
+      for (int i4 = 0; i4 < 4; ++i4)
+        store4(TO{}, ot + c * RB + 16 * ((4 * db + i4) ^ (c % NCO)) + 8 * h,
+               oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv,
+               oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
+    wave_lds_sync();
+    constexpr int RPI = 64 / NCO;  // rows per store instruction
+    const int rr = lane / NCO, ch = lane % NCO;
+#pragma unroll
+    for (int i = 0; i < 32 / RPI; ++i) {
+      const int r = RPI * i + rr;
+      const u32x4 v = lds16(ot + r * RB + 16 * (ch ^ (r % NCO)));
+      if (qw0 + r < p.Sq) *(u32x4*)(out_row(qw0 + r) + 16 * ch) = v;
     }
-  if (h == 0) {
+  } else if (q_ok) {
+    char* orow = out_row(qi);
+#pragma unroll
+    for (int db = 0; db < D / 32; ++db)
+#pragma unroll
+      for (int i4 = 0; i4 < 4; ++i4) {
+        const int d = 32 * db + 8 * i4 + 4 * h;
+        store4(TO{}, orow + d * OB, oacc[db][4 * i4] * inv, oacc[db][4 * i4 + 1] * inv,
+               oacc[db][4 * i4 + 2] * inv, oacc[db][4 * i4 + 3] * inv);
+      }
+  }
+  if (q_ok && h == 0) {
     if (S == 1) {
       if (p.lse) p.lse[((int64_t)b * p.Hq + hq) * p.Sq + qi] = lse;
     } else {
-      p.part_lse[prow] = lse;
+      p.part_lse[(int64_t)split * p.B * p.Sq * p.Hq + ((int64_t)b * p.Sq + qi) * p.Hq + hq] = lse;
     }
   }
 }
