@@ -379,24 +379,53 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
     l_tot = l_tot * a0 + l1 * a1;
     m_run = m;
   }
-  if (!hvalid) return;
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   const float lse = l_tot > 0.f ? m_run * p.scale + __logf(l_tot) : -INFINITY;
   // The output row ([B, Sq, Hq] order), or with several splits this split's
   // partial row (same 16-bit type; the combine weighs the partials by their
-  // lse and writes lse as [B, Hq, Sq]).
-  const int64_t row = ((int64_t)b * p.Sq + qtok) * p.Hq + head;
-  const int64_t prow = S == 1 ? row : (int64_t)split * p.B * p.Sq * p.Hq + row;
-  char* orow = (char*)(S == 1 ? p.o : p.part_o) + (prow * MLA_DV + MLA_DVW * kh) * 2;
+  // lse and writes lse as [B, Hq, Sq]). Row rig of the workgroup is new token
+  // rig % Sq and head rig / Sq.
+  char* obase = (char*)(S == 1 ? p.o : p.part_o) +
+                (S == 1 ? 0 : (int64_t)split * p.B * p.Sq * p.Hq * MLA_DV * 2);
+  auto out_half = [&](int r) {  // this wave's half of row r's columns
+    return obase + ((((int64_t)b * p.Sq + r % p.Sq) * p.Hq + r / p.Sq) * MLA_DV + MLA_DVW * kh) * 2;
+  };
+  if constexpr (NH == 64) {
+    // Through LDS: a lane holds 4 columns of one head per store, so direct
+    // stores would touch the wave's 16 rows per instruction. Each wave writes
+    // its 16 half rows (512 bytes each; 16-byte chunk q of row j at chunk
+    // q ^ j) into its own 8 KB of the idle stages and stores two half rows per
+    // instruction.
+    lds_barrier();  // every wave is done with the stages
+    char* ot = smem + 8192 * w;
 #pragma unroll
-  for (int db = 0; db < NPV; ++db) {
-    const u32x2 v{T::pack2(oacc[db][0] * inv, oacc[db][1] * inv),
-                  T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
-    *(u32x2*)(orow + (16 * db + 4 * gq) * 2) = v;
+    for (int db = 0; db < NPV; ++db) {
+      const u32x2 v{T::pack2(oacc[db][0] * inv, oacc[db][1] * inv),
+                    T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
+      *(u32x2*)(ot + 512 * c16 + 16 * ((2 * db + (gq >> 1)) ^ c16) + 8 * (gq & 1)) = v;
+    }
+    wave_lds_sync();
+    const int jj = lane >> 5, ch = lane & 31;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int j = 2 * i + jj;
+      const u32x4 v = lds16(ot + 512 * j + 16 * (ch ^ j));
+      const int r = hb * NH + 16 * hg + j;
+      if (r / p.Sq < p.Hq) *(u32x4*)(out_half(r) + 16 * ch) = v;
+    }
+  } else if (hvalid) {
+    char* orow = out_half(rig);
+#pragma unroll
+    for (int db = 0; db < NPV; ++db) {
+      const u32x2 v{T::pack2(oacc[db][0] * inv, oacc[db][1] * inv),
+                    T::pack2(oacc[db][2] * inv, oacc[db][3] * inv)};
+      *(u32x2*)(orow + (16 * db + 4 * gq) * 2) = v;
+    }
   }
-  if (gq == 0 && kh == 0) {
+  if (hvalid && gq == 0 && kh == 0) {
+    const int64_t row = ((int64_t)b * p.Sq + qtok) * p.Hq + head;
     if (S > 1)
-      p.part_lse[prow] = lse;
+      p.part_lse[(int64_t)split * p.B * p.Sq * p.Hq + row] = lse;
     else if (p.lse)
       p.lse[((int64_t)b * p.Hq + head) * p.Sq + qtok] = lse;
   }
