@@ -121,57 +121,64 @@ __global__ __launch_bounds__(256) void combine_kernel(CombineParams p) {
 
 // Few rows, many splits (decode of a small batch): one 256-thread block per
 // row. Thread (sg, col) handles output columns 4 col .. 4 col + 3 for the
-// splits s = sg, sg + SG, ...; the per-thread partial sums are then added up
-// over the SG split groups through LDS.
+// splits s = sg, sg + SG, ..., eight at a time with all of a batch's loads
+// issued together and a running maximum of lse (as in combine_one); the SG
+// split groups' (max, sum, columns) are then merged through LDS.
 template <typename TO, int TPR, bool P16>
 __global__ __launch_bounds__(256) void combine_row_kernel(CombineParams p) {
   constexpr int SG = 256 / TPR;
-  __shared__ float red[256];
+  constexpr int NB = 8;
   __shared__ f32x4 racc[SG][TPR];
-  __shared__ float rsum[SG][TPR];
+  __shared__ float rsum[SG][TPR], rmax[SG][TPR];
   const int row = blockIdx.x, tid = threadIdx.x;
   const int sg = tid / TPR, col = tid % TPR, d = 4 * col;
   const int S = p.n_splits;
   const int64_t rows = p.rows;
   const float* lse_p = p.part_lse + row;
-  float m = -INFINITY;
-  for (int s = tid; s < S; s += 256) m = fmaxf(m, lse_p[s * rows]);
-  red[tid] = m;
-  __syncthreads();
-  for (int k = 128; k > 0; k >>= 1) {
-    if (tid < k) red[tid] = fmaxf(red[tid], red[tid + k]);
-    __syncthreads();
-  }
-  const float mx = red[0];
+  const int64_t o_i = (int64_t)row * p.D + d;
+  const int64_t o_stride = rows * p.D;
   f32x4 acc = f32x4{};
-  float sum = 0.f;
-  if (mx != -INFINITY) {
-    const int64_t o_i = (int64_t)row * p.D + d;
-    const int64_t o_stride = rows * p.D;
-    for (int s0 = sg; s0 < S; s0 += 4 * SG) {
-      float l[4];
-      f32x4 o[4];
+  float m = -INFINITY, sum = 0.f;
+  for (int s0 = sg; s0 < S; s0 += NB * SG) {
+    float l[NB];
+    f32x4 o[NB];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int s = min(s0 + u * SG, S - 1);
-        l[u] = s0 + u * SG < S ? lse_p[s * rows] : -INFINITY;
-        o[u] = load_part4<TO, P16>(p.part_o, o_i + s * o_stride);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const float wgt = __expf(l[u] - mx);  // 0 for an empty split (lse -inf)
-        sum += wgt;
-        if (wgt != 0.f) acc += wgt * o[u];
-      }
+    for (int u = 0; u < NB; ++u) {
+      const int s = min(s0 + u * SG, S - 1);
+      l[u] = s0 + u * SG < S ? lse_p[s * rows] : -INFINITY;
+      o[u] = load_part4<TO, P16>(p.part_o, o_i + s * o_stride);
     }
+    float m_new = m;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) m_new = fmaxf(m_new, l[u]);
+    // Reference point 0 while every split so far is empty (lse -inf).
+    const float m_ref = m_new == -INFINITY ? 0.f : m_new;
+    const float r = __expf(m - m_ref);  // 0 while m is -inf
+    sum *= r;
+    acc *= r;
+#pragma unroll
+    for (int u = 0; u < NB; ++u) {
+      const float wgt = __expf(l[u] - m_ref);  // 0 for an empty split
+      sum += wgt;
+      if (wgt != 0.f) acc += wgt * o[u];
+    }
+    m = m_new;
   }
   racc[sg][col] = acc;
   rsum[sg][col] = sum;
+  rmax[sg][col] = m;
   __syncthreads();
   if (sg != 0) return;
+  float mx = m;
+  for (int k = 1; k < SG; ++k) mx = fmaxf(mx, rmax[k][col]);
+  const float mx_ref = mx == -INFINITY ? 0.f : mx;
+  const float w0 = __expf(m - mx_ref);  // each group's sums are relative to its own max
+  acc *= w0;
+  sum *= w0;
   for (int k = 1; k < SG; ++k) {
-    acc += racc[k][col];
-    sum += rsum[k][col];
+    const float wk = __expf(rmax[k][col] - mx_ref);
+    acc += wk * racc[k][col];
+    sum += wk * rsum[k][col];
   }
   const float inv = sum > 0.f ? 1.f / sum : 0.f;
   acc *= inv;
