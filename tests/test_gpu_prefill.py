@@ -96,7 +96,11 @@ def test_prefill_split_sweep(fa, splits, causal, monkeypatch):
     assert_lse(to_f64(lse), ref_lse, f"splits={splits}")
 
 
-WAVE_SHAPES = [s for s in SMALL if s[5] == 128] + [(1, 4, 2, 600, 2000, 128, True, "bf16", "bf16")]
+WAVE_SHAPES = [s for s in SMALL if s[5] == 128] + [
+    (1, 4, 2, 600, 2000, 128, True, "bf16", "bf16"),
+    # fp32 output: rows (and fp32 split partials) stored directly, not through LDS
+    (1, 4, 2, 333, 900, 128, True, "bf16", "fp32"),
+]
 
 
 @pytest.mark.parametrize("waves", ["4", "8"])
