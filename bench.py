@@ -166,7 +166,7 @@ def main():
     o3 = torch.empty_like(q3)
     Hq, Hkv, D, S = inp3.Hq, inp3.Hkv, inp3.D, inp3.Sq
     n_ub = S // UB
-    ws3_bytes = max(fa.fa_prefill_workspace_size(1, Hq, Hkv, UB, UB * (u + 1), D, 1)
+    ws3_bytes = max(fa.fa_prefill_workspace_size(1, Hq, Hkv, UB, UB * (u + 1), D, 1, fa.FA_BF16)
                     for u in range(n_ub))
     ws3 = torch.empty(max(ws3_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
     ub_args = [(q3[:, UB * u:UB * (u + 1)], k3[:, :UB * (u + 1)], v3[:, :UB * (u + 1)],
@@ -213,6 +213,39 @@ def main():
                                                   16, inp5.max_seq_len, fa.FA_KV_SPLIT)
     ws5 = torch.empty(max(ws5_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
 
+    # Workload 2: non-causal MHA prefill, B=4, 16 heads, 2048 tokens, D=64, bf16
+    # (one fa_prefill_ex call, planner-chosen workgroups and splits).
+    inp2 = fi.workload(2)
+    q2, k2, v2 = to_dev(inp2.q), to_dev(inp2.k), to_dev(inp2.v)
+    o2 = torch.empty_like(q2)
+    ws2_bytes = fa.fa_prefill_workspace_size(inp2.B, inp2.Hq, inp2.Hkv, inp2.Sq, inp2.Skv,
+                                             inp2.D, 0, fa.FA_BF16)
+    ws2 = torch.empty(max(ws2_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
+
+    def mha_pass():
+        fa.fa_prefill_ex(q2, k2, v2, o2, None, inp2.B, inp2.Hq, inp2.Hkv, inp2.Sq, inp2.Skv,
+                         inp2.D, 0, inp2.scale, fa.FA_BF16, fa.FA_BF16, ws2, ws2_bytes,
+                         stream=sid)
+
+    # Workload 5: small-batch GQA decode, one new token per sequence (4 sequences of
+    # U[1024, 32768] tokens, 32 query / 8 K/V heads, D=128, page 16).
+    inp5s = fi.workload(5)
+    q5s, pool5s = to_dev(inp5s.q), to_dev(inp5s.pool)
+    pt5s = torch.from_numpy(inp5s.page_table).to(dev)
+    sl5s = torch.from_numpy(inp5s.seq_lens).to(dev)
+    o5s = torch.empty((inp5s.B, inp5s.Hq, 128), dtype=torch.bfloat16, device=dev)
+    ws5s_bytes = fa.fa_decode_workspace_size(inp5s.B, inp5s.Hq, inp5s.Hkv, 128, 128, 16,
+                                             inp5s.max_seq_len, fa.FA_KV_SPLIT)
+    ws5s = torch.empty(max(ws5s_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
+    n_split5s = fa.fa_decode_num_splits(inp5s.B, inp5s.Hq, inp5s.Hkv, 128, 128, 16,
+                                        inp5s.max_seq_len, fa.FA_KV_SPLIT)
+
+    def decode_gqa_pass():
+        fa.fa_decode_paged(q5s, pool5s, pt5s, sl5s, pool5s.shape[0], o5s, None, inp5s.B,
+                           inp5s.Hq, inp5s.Hkv, 128, 128, 16, inp5s.max_pages,
+                           inp5s.max_seq_len, fa.FA_KV_SPLIT, inp5s.scale, 0, fa.FA_BF16, ws5s,
+                           ws5s_bytes, stream=sid)
+
     # Workload 4 decoding 2 new tokens per sequence at once (the same pool and table).
     q4m = to_dev(fi.normal_bits((inp4.B, 2, inp4.Hq, 576), "bf16", fi.rng_for(4, fi.T_Q)))
     o4m = torch.empty((inp4.B, 2, inp4.Hq, 512), dtype=torch.bfloat16, device=dev)
@@ -221,19 +254,19 @@ def main():
     ws4m = torch.empty(max(ws4m_bytes, 16) // 4 + 4, dtype=torch.float32, device=dev)
 
     def decode_mla_multi_pass():
-        fa.fa_decode_paged_multi(q4m, pool4, pool4.shape[0], pt4, sl4, o4m, None, inp4.B, 2,
+        fa.fa_decode_paged_multi(q4m, pool4, pt4, sl4, pool4.shape[0], o4m, None, inp4.B, 2,
                                  inp4.Hq, 1, 576, 512, 1, inp4.max_pages, inp4.max_seq_len,
                                  fa.FA_KV_MLA_SHARED, inp4.scale, 0, fa.FA_BF16, ws4m,
                                  ws4m_bytes, stream=sid)
 
     def decode_multi_pass():
-        fa.fa_decode_paged_multi(q5, pool5, pool5.shape[0], pt5, sl5, o5, None, inp5.B, inp5.Sq,
+        fa.fa_decode_paged_multi(q5, pool5, pt5, sl5, pool5.shape[0], o5, None, inp5.B, inp5.Sq,
                                  inp5.Hq, inp5.Hkv, 128, 128, 16, inp5.max_pages,
                                  inp5.max_seq_len, fa.FA_KV_SPLIT, inp5.scale, 0, fa.FA_BF16,
                                  ws5, ws5_bytes, stream=sid)
 
     def decode_pass():
-        fa.fa_decode_paged(q4, pool4, pool4.shape[0], pt4, sl4, o4, None, inp4.B, inp4.Hq, 1, 576,
+        fa.fa_decode_paged(q4, pool4, pt4, sl4, pool4.shape[0], o4, None, inp4.B, inp4.Hq, 1, 576,
                            512, 1, inp4.max_pages, inp4.max_seq_len, fa.FA_KV_MLA_SHARED,
                            inp4.scale, 0, fa.FA_BF16, ws4, ws4_bytes, stream=sid)
 
@@ -300,6 +333,19 @@ def main():
         torch.cuda.synchronize()
         return sum(e0.elapsed_time(e1) for e0, e1 in evs) / 1e3
 
+    def timed_warm(fn):
+        for _ in range(2):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / 1e3
+
+    t_mha = timed_warm(mha_pass)
+    t_d5s = timed_cold(decode_gqa_pass)
     t_d5 = timed_cold(decode_multi_pass)
     t_d4m = timed_cold(decode_mla_multi_pass)
 
@@ -369,6 +415,51 @@ def main():
         },
         "cpu_baseline": None,
     }
+    flops2 = 4 * inp2.B * inp2.Hq * inp2.Sq * inp2.Skv * inp2.D
+    mha_tflops = flops2 * K / t_mha / 1e12
+    result["prefill_mha"] = {
+        "metric": "non-causal MHA prefill attn TFLOP/s (%MFMA peak)",
+        "value": round(mha_tflops, 2),
+        "unit": "TFLOP/s",
+        "us_per_call": round(t_mha / K * 1e6, 2),
+        "flop_per_call": flops2,
+        "workload": "non-causal MHA B=4 Hq=Hkv=16 Sq=Skv=2048 D=64 bf16, scale 1/8; warm "
+                    "(inputs resident, back-to-back calls)",
+        "splits": max(1, ws2_bytes // (inp2.B * inp2.Sq * inp2.Hq * (inp2.D * 2 + 4))),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(mha_tflops, 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(mha_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "fa_prefill_ex call (prefill kernel, plus the split combine if the "
+                      "planner splits)",
+        },
+    }
+    bytes5s = split_decode_bytes(inp5s)
+    d5s_gbs = bytes5s * K / t_d5s / 1e9
+    result["decode_gqa"] = {
+        "metric": "small-batch paged GQA decode GB/s (%HBM peak)",
+        "value": round(d5s_gbs, 1),
+        "unit": "GB/s",
+        "us_per_call": round(t_d5s / K * 1e6, 2),
+        "bytes_per_call": bytes5s,
+        "workload": "4 sequences of U[1024, 32768] tokens (seeded: "
+                    + "/".join(str(int(n)) for n in inp5s.seq_lens)
+                    + "), 32 query / 8 K/V heads, D=128, page 16, one new token each, bf16; "
+                      "cold (after a cache-evicting read)",
+        "splits": n_split5s,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(d5s_gbs, 1),
+            "peak": PEAK_HBM_GBS,
+            "unit": "GB/s",
+            "frac": round(d5s_gbs / PEAK_HBM_GBS, 4),
+            "traffic": None,
+            "kernel": "fa_decode_paged call (GQA decode kernel + split combine)",
+        },
+    }
     bytes5 = split_decode_bytes(inp5)
     d5_gbs = bytes5 * K / t_d5 / 1e9
     result["decode_multi"] = {
@@ -423,7 +514,7 @@ def main():
             ws_ps = torch.empty(max(wsb_ps, 16) // 4 + 4, dtype=torch.float32, device=dev)
 
             def ps_pass():
-                fa.fa_decode_paged(q_ps, pool_ps, pool_ps.shape[0], pt_ps, sl_ps, o4, None, 128,
+                fa.fa_decode_paged(q_ps, pool_ps, pt_ps, sl_ps, pool_ps.shape[0], o4, None, 128,
                                    64, 1, 576, 512, ps, inp_ps.max_pages, 2048,
                                    fa.FA_KV_MLA_SHARED, inp_ps.scale, 0, fa.FA_BF16, ws_ps,
                                    wsb_ps, stream=sid)

@@ -57,12 +57,12 @@ _L = ctypes.c_int64
 _lib.fa_prefill_mask.argtypes = [_P, _P, _P, _P, _L, _L, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F,
                                  _I, _I, _P, _Z, _P]
 _lib.fa_prefill_mask.restype = _I
-_lib.fa_prefill_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I]
+_lib.fa_prefill_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I]
 _lib.fa_prefill_workspace_size.restype = _Z
-_lib.fa_decode_paged.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
+_lib.fa_decode_paged.argtypes = [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _I, _F,
                                  _I, _I, _P, _Z, _P]
 _lib.fa_decode_paged.restype = _I
-_lib.fa_decode_paged_multi.argtypes = [_P, _P, _I, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+_lib.fa_decode_paged_multi.argtypes = [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I,
                                        _I, _I, _I, _F, _I, _I, _P, _Z, _P]
 _lib.fa_decode_paged_multi.restype = _I
 _lib.fa_decode_multi_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I, _I]
@@ -145,31 +145,32 @@ def fa_prefill_mask(q, k, v, mask, mask_stride, mask_batch_stride, o, lse, B, Hq
                                 _stream(stream)), "fa_prefill_mask")
 
 
-def fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal) -> int:
-    return int(_lib.fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, int(bool(causal))))
+def fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal, out_dtype) -> int:
+    return int(_lib.fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, int(bool(causal)),
+                                              int(out_dtype)))
 
 
-def fa_decode_paged(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Hq, Hkv, D_qk, D_v,
+def fa_decode_paged(q, kv_pool, page_table, seq_lens, num_pages, o, lse, B, Hq, Hkv, D_qk, D_v,
                     page_size, max_pages_per_seq, max_seq_len, layout, scale, num_splits, dtype,
                     workspace=None, workspace_bytes=0, stream=None) -> None:
     if workspace is not None and not isinstance(workspace, int) and not workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib.fa_decode_paged(_ptr(q), _ptr(kv_pool), int(num_pages), _ptr(page_table),
-                                _ptr(seq_lens),
-                                _ptr(o), _ptr(lse), B, Hq, Hkv, D_qk, D_v, page_size,
+    _check(_lib.fa_decode_paged(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(seq_lens),
+                                int(num_pages), _ptr(o), _ptr(lse), B, Hq, Hkv, D_qk, D_v,
+                                page_size,
                                 max_pages_per_seq, max_seq_len, int(layout), float(scale),
                                 int(num_splits), int(dtype), _ptr(workspace),
                                 int(workspace_bytes), _stream(stream)), "fa_decode_paged")
 
 
-def fa_decode_paged_multi(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Sq, Hq, Hkv,
+def fa_decode_paged_multi(q, kv_pool, page_table, seq_lens, num_pages, o, lse, B, Sq, Hq, Hkv,
                           D_qk, D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale,
                           num_splits, dtype, workspace=None, workspace_bytes=0,
                           stream=None) -> None:
     if workspace is not None and not isinstance(workspace, int) and not workspace_bytes:
         workspace_bytes = workspace.numel() * workspace.element_size()
-    _check(_lib.fa_decode_paged_multi(_ptr(q), _ptr(kv_pool), int(num_pages), _ptr(page_table),
-                                      _ptr(seq_lens), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv, D_qk,
+    _check(_lib.fa_decode_paged_multi(_ptr(q), _ptr(kv_pool), _ptr(page_table), _ptr(seq_lens),
+                                      int(num_pages), _ptr(o), _ptr(lse), B, Sq, Hq, Hkv, D_qk,
                                       D_v, page_size, max_pages_per_seq, max_seq_len,
                                       int(layout), float(scale), int(num_splits), int(dtype),
                                       _ptr(workspace), int(workspace_bytes), _stream(stream)),
@@ -232,7 +233,8 @@ def prefill(q, k, v, *, causal: bool, scale: Optional[float] = None, out=None, o
     if out is None:
         out = torch.empty((B, Sq, Hq, D), dtype=out_dtype or q.dtype, device=q.device)
     lse = torch.empty((B, Hq, Sq), dtype=torch.float32, device=q.device) if return_lse else None
-    ws = _workspace(fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal), q.device) \
+    ws = _workspace(fa_prefill_workspace_size(B, Hq, Hkv, Sq, Skv, D, causal,
+                                              _fa_dtype(out.dtype)), q.device) \
         if allow_split else None
     wsb = 0 if ws is None else ws.numel() * 4
     if mask is None:
@@ -277,7 +279,7 @@ def decode_paged(q, kv_pool, page_table, seq_lens, *, layout: int, scale: float,
         workspace = _workspace(fa_decode_workspace_size(B, Hq, Hkv, D_qk, D_v, page_size,
                                                         max_seq_len, layout, num_splits),
                                q.device)
-    fa_decode_paged(q, kv_pool, kv_pool.shape[0], page_table, seq_lens, out, lse, B, Hq, Hkv,
+    fa_decode_paged(q, kv_pool, page_table, seq_lens, kv_pool.shape[0], out, lse, B, Hq, Hkv,
                     D_qk, D_v, page_size,
                     page_table.shape[1], max_seq_len, layout, scale, num_splits,
                     _fa_dtype(q.dtype), workspace,
@@ -303,7 +305,7 @@ def _decode_multi(q, kv_pool, page_table, seq_lens, *, layout, scale, max_seq_le
         workspace = _workspace(fa_decode_multi_workspace_size(B, Sq, Hq, Hkv, D_qk, D_v, page_size,
                                                               max_seq_len, layout, num_splits),
                                q.device)
-    fa_decode_paged_multi(q, kv_pool, kv_pool.shape[0], page_table, seq_lens, out, lse, B, Sq, Hq,
+    fa_decode_paged_multi(q, kv_pool, page_table, seq_lens, kv_pool.shape[0], out, lse, B, Sq, Hq,
                           Hkv, D_qk, D_v, page_size, page_table.shape[1], max_seq_len, layout,
                           scale, num_splits, _fa_dtype(q.dtype), workspace,
                           0 if workspace is None else workspace.numel() * workspace.element_size(),

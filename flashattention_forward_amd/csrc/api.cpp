@@ -7,6 +7,7 @@
 // compute unit (the occupancy bug there launched too few), and size tiles to the
 // chip (here 160 KiB of LDS and 256 CUs of MI355X).
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cmath>
 #include <cstdint>
@@ -20,15 +21,35 @@ using namespace fa;
 
 namespace {
 
-// Compute units the planner targets. gfx950 parts (MI350X / MI355X) have 256;
-// planning never queries the device, so workspace sizes are pure functions of
-// the shape. FA_NUM_CUS overrides it for experiments.
+int env_int(const char* name, int dflt);
+
+// Compute units the planner sizes grids for: those of the current device, read
+// once per device with hipDeviceGetAttribute and cached (a racing first query
+// stores the same value). FA_NUM_CUS overrides it; with no usable device (a
+// host-only process asking for workspace sizes) the 256 of MI355X are assumed.
+// Workspace sizes therefore hold for the device that is current when they are
+// asked for, which must be the one the matching call runs on.
+constexpr int kDefaultCus = 256;
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_device_cus[kMaxDevices];
+
 int planner_cus() {
-  static int cus = [] {
-    const char* e = std::getenv("FA_NUM_CUS");
-    int v = e ? std::atoi(e) : 256;
-    return v > 0 ? v : 256;
-  }();
+  const int forced = env_int("FA_NUM_CUS", 0);
+  if (forced > 0) return forced;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    (void)hipGetLastError();  // do not leave the failed query for a later launch check
+    return kDefaultCus;
+  }
+  int cus = g_device_cus[dev].load(std::memory_order_relaxed);
+  if (cus <= 0) {
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        cus <= 0) {
+      (void)hipGetLastError();
+      cus = kDefaultCus;
+    }
+    g_device_cus[dev].store(cus, std::memory_order_relaxed);
+  }
   return cus;
 }
 
@@ -65,7 +86,10 @@ int prefill_splits(int64_t base, int max_tiles, int waves) {
   return S;
 }
 
-PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split) {
+// out_bytes: bytes per element of the output type, which the split partials
+// share (2 for bf16/fp16, 4 for fp32).
+PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split,
+                         int out_bytes) {
   PrefillPlan pl;
   const int max_tiles = ceil_div(Skv, PF_BN);
   // Head size 128 uses 8-wave workgroups when they (with splits) still give
@@ -88,7 +112,9 @@ PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split
     S = std::max(1, std::min(S, std::max(1, max_tiles)));
   }
   pl.n_splits = S;
-  if (S > 1) pl.ws_bytes = (size_t)S * B * Sq * Hq * (size_t)(D + 1) * sizeof(float);
+  // Per split: the partial rows in the output type and an fp32 lse per row.
+  if (S > 1)
+    pl.ws_bytes = (size_t)S * B * Sq * Hq * ((size_t)D * out_bytes + sizeof(float));
   return pl;
 }
 
@@ -129,11 +155,14 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
   } else {
     pl.n_hblk = ceil_div((Hq / Hkv) * Sq, 16);  // rows: new tokens x heads of a group
     units = (int64_t)B * Hkv * pl.n_hblk;  // one wave per unit
-    // Four waves per SIMD: the splits past a shorter sequence's end (about
-    // half of them for lengths uniform up to max_seq_len) exit at once, and a
-    // wave keeps one tile in flight, so shorter chains of tiles pay. (4
-    // sequences of 1.8K-23K tokens, 32/8 heads: 92 splits of 256 tokens take
-    // 50 us against 59 us for 62 of 384.)
+    // 16 waves per CU, twice the 8 that are resident at a time (the kernel's
+    // 180 VGPRs + 36 AGPRs leave room for two waves per SIMD): in a ragged
+    // batch the splits past a shorter sequence's end (about half of them for
+    // lengths uniform up to max_seq_len) exit at once without holding a slot,
+    // and a wave keeps one tile in flight, so shorter chains of tiles pay.
+    // Measured on 4 sequences of 1.8K-23K tokens, 32/8 heads: 92 splits of 256
+    // tokens take 50 us against 59 us for 62 of 384 (a grid sized to the
+    // resident waves).
     target = 16 * (int64_t)planner_cus();
   }
   int S = 1;
@@ -198,11 +227,13 @@ const char* fa_strerror(int status) {
   }
 }
 
-size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal) {
+size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D, int causal,
+                                 fa_dtype out_dtype) {
   (void)Hkv;
   (void)causal;
   if (B < 1 || Hq < 1 || Sq < 1 || Skv < 0 || (D != 64 && D != 128)) return 0;
-  return plan_prefill(B, Hq, Sq, Skv, D, true).ws_bytes;
+  if (out_dtype != FA_BF16 && out_dtype != FA_FP16 && out_dtype != FA_FP32) return 0;
+  return plan_prefill(B, Hq, Sq, Skv, D, true, out_dtype == FA_FP32 ? 4 : 2).ws_bytes;
 }
 
 static int prefill_impl(const void* q, const void* k, const void* v, const void* mask,
@@ -214,7 +245,8 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
   if (rc != FA_OK) return rc;
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
   if (Sq == 0) return FA_OK;
-  const PrefillPlan pl = plan_prefill(B, Hq, Sq, Skv, D, workspace != nullptr);
+  const int out_bytes = out_dtype == FA_FP32 ? 4 : 2;
+  const PrefillPlan pl = plan_prefill(B, Hq, Sq, Skv, D, workspace != nullptr, out_bytes);
   if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
   if ((int64_t)B * Hq * pl.n_qtiles * pl.n_splits > kMaxGrid) return FA_ERR_SHAPE;
   if (pl.n_splits > 1 && (int64_t)B * Sq * Hq > INT_MAX) return FA_ERR_SHAPE;
@@ -245,8 +277,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
   const int64_t rows = (int64_t)B * Sq * Hq;
   if (pl.n_splits > 1) {
     p.part_o = workspace;
-    p.part_lse = (float*)((char*)workspace +
-                          (size_t)pl.n_splits * rows * D * (out_dtype == FA_FP32 ? 4 : 2));
+    p.part_lse = (float*)((char*)workspace + (size_t)pl.n_splits * rows * D * out_bytes);
   }
   const InType it = in_dtype == FA_BF16 ? InType::bf16 : InType::f16;
   const OutType ot = out_dtype == FA_BF16 ? OutType::bf16
@@ -451,19 +482,18 @@ static int decode_impl(const void* q, const void* kv_pool, int num_pages,
   return FA_OK;
 }
 
-int fa_decode_paged(const void* q, const void* kv_pool, int num_pages,
-                    const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
-                    int B, int Hq, int Hkv,
-                    int D_qk, int D_v, int page_size, int max_pages_per_seq, int max_seq_len,
-                    fa_kv_layout layout, float scale, int num_splits, fa_dtype dtype,
-                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+int fa_decode_paged(const void* q, const void* kv_pool, const int32_t* page_table,
+                    const int32_t* seq_lens, int num_pages, void* o, float* lse, int B, int Hq,
+                    int Hkv, int D_qk, int D_v, int page_size, int max_pages_per_seq,
+                    int max_seq_len, fa_kv_layout layout, float scale, int num_splits,
+                    fa_dtype dtype, void* workspace, size_t workspace_bytes, hipStream_t stream) {
   return decode_impl(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, 1, Hq, Hkv, D_qk,
                      D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale, num_splits,
                      dtype, workspace, workspace_bytes, stream);
 }
 
-int fa_decode_paged_multi(const void* q, const void* kv_pool, int num_pages,
-                          const int32_t* page_table, const int32_t* seq_lens, void* o, float* lse,
+int fa_decode_paged_multi(const void* q, const void* kv_pool, const int32_t* page_table,
+                          const int32_t* seq_lens, int num_pages, void* o, float* lse,
                           int B, int Sq, int Hq, int Hkv, int D_qk, int D_v, int page_size,
                           int max_pages_per_seq, int max_seq_len, fa_kv_layout layout,
                           float scale, int num_splits, fa_dtype dtype, void* workspace,

@@ -208,14 +208,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        float e = fast_exp2(fmaf(sacc[kb][i], sl2, nb));
-        if (tail && tt + 16 * kb + 4 * gq + i >= t1) e = 0.f;
-        pv[kb][i] = e;
-        l_run += e;
-      }
+      for (int i = 0; i < 4; ++i) pv[kb][i] = fast_exp2(fmaf(sacc[kb][i], sl2, nb));
     const u32x4 pb{T::pack2(pv[0][0], pv[0][1]), T::pack2(pv[0][2], pv[0][3]),
                    T::pack2(pv[1][0], pv[1][1]), T::pack2(pv[1][2], pv[1][3])};
+    // The row sum is taken over the 16-bit probabilities the P V product uses,
+    // so the output's weights are exactly the ones it is normalised by.
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) l_run = T::sum2(pb[q4], l_run);
     const int j = c16;
     const char* va = vlds + ((4 * gq + (j >> 2)) * DS_VS + 4 * (j & 3)) * 2;
 #pragma unroll

@@ -29,7 +29,7 @@ struct PrefillParams {
   float scale_log2;  // |scale| * log2(e)
   // Explicit additive mask (input type) or null: element (b, i, j) at
   // mask[b * mask_bstride + i * mask_stride + j]; mask_stride and mask_bstride
-  // are multiples of 4 and rows hold at least Skv rounded up to 4 elements.
+  // are multiples of 8 and rows hold at least Skv rounded up to 8 elements.
   const void* mask;
   int64_t mask_bstride, mask_stride;
 };

@@ -31,6 +31,37 @@ def test_header_declares_entry_points():
         assert n in names
 
 
+def declared_params(name):
+    """Parameter names of one declaration in fa.h, in order."""
+    text = re.sub(r"/\*.*?\*/", "", open(HEADER).read(), flags=re.S)
+    m = re.search(r"\b" + name + r"\s*\(([^)]*)\)\s*;", text)
+    assert m, f"{name} not declared"
+    return [re.findall(r"(\w+)\s*$", p.strip())[0] for p in m.group(1).split(",")]
+
+
+def test_north_star_argument_order():
+    """The two calls the path is specified by keep their argument lists:
+    fa_prefill(q,k,v,o,B,Hq,Hkv,Sq,Skv,D,causal,scale,stream) exactly, and
+    fa_decode_paged(q,kv_pool,page_table,seq_lens,...,stream)."""
+    assert declared_params("fa_prefill") == ["q", "k", "v", "o", "B", "Hq", "Hkv", "Sq", "Skv",
+                                             "D", "causal", "scale", "stream"]
+    for name in ("fa_decode_paged", "fa_decode_paged_multi"):
+        ps = declared_params(name)
+        assert ps[:4] == ["q", "kv_pool", "page_table", "seq_lens"], (name, ps)
+        assert ps[-1] == "stream"
+
+
+def test_binding_argument_counts(fa):
+    """The ctypes binding passes as many arguments as the header declares."""
+    import flashattention_forward_amd as pkg
+    for name in declared_functions():
+        fn = getattr(pkg._lib, name)
+        n = len(declared_params(name))
+        if declared_params(name) == ["void"]:
+            n = 0
+        assert len(fn.argtypes) == n, f"{name}: binding {len(fn.argtypes)} vs header {n}"
+
+
 def test_library_exports_every_declared_symbol(fa):
     lib = ctypes.CDLL(fa.LIB_PATH)
     for n in declared_functions():
@@ -71,7 +102,7 @@ def test_prefill_mask_validation(fa):
 def test_decode_multi_validation(fa):
     def call(Sq=4, layout=None, Dqk=128, Dv=128, Hkv=2):
         lay = fa.FA_KV_SPLIT if layout is None else layout
-        return fa.fa_decode_paged_multi(A, A, 8, A, A, A, None, 2, Sq, 8, Hkv, Dqk, Dv, 16, 4, 64,
+        return fa.fa_decode_paged_multi(A, A, A, A, 8, A, None, 2, Sq, 8, Hkv, Dqk, Dv, 16, 4, 64,
                                         lay, 0.1, 0, fa.FA_BF16, None, 0, stream=0)
 
     assert _err(call, Sq=0) == -2
@@ -113,7 +144,7 @@ def test_prefill_validation(fa):
     assert _err(call, ws=A + 4) == -4
     # a plan that splits the keys needs the full workspace
     big = dict(B=1, Hq=4, Hkv=4, Sq=128, Skv=8192, D=128)
-    need = fa.fa_prefill_workspace_size(1, 4, 4, 128, 8192, 128, 0)
+    need = fa.fa_prefill_workspace_size(1, 4, 4, 128, 8192, 128, 0, fa.FA_BF16)
     assert need > 0
     assert _err(call, ws=A, ws_bytes=need - 4, **big) == -5
     # nothing to do: returns before any launch
@@ -122,11 +153,16 @@ def test_prefill_validation(fa):
 
 
 def test_prefill_workspace_size_rules(fa):
-    assert fa.fa_prefill_workspace_size(1, 32, 8, 512, 512, 128, 1) == 0  # short keys: no split
-    ws = fa.fa_prefill_workspace_size(1, 32, 8, 512, 16384, 128, 1)
+    # short keys: no split
+    assert fa.fa_prefill_workspace_size(1, 32, 8, 512, 512, 128, 1, fa.FA_BF16) == 0
     rows = 512 * 32
-    assert ws % (rows * 129 * 4) == 0 and ws // (rows * 129 * 4) in (2, 4, 8, 16)
-    assert fa.fa_prefill_workspace_size(0, 1, 1, 1, 1, 64, 0) == 0
+    # per split: partial rows in the output type and an fp32 lse per row
+    for dt, per_row in ((fa.FA_BF16, 128 * 2 + 4), (fa.FA_FP16, 128 * 2 + 4),
+                        (fa.FA_FP32, 128 * 4 + 4)):
+        ws = fa.fa_prefill_workspace_size(1, 32, 8, 512, 16384, 128, 1, dt)
+        assert ws % (rows * per_row) == 0 and ws // (rows * per_row) in (2, 4, 8, 16)
+    assert fa.fa_prefill_workspace_size(0, 1, 1, 1, 1, 64, 0, fa.FA_BF16) == 0
+    assert fa.fa_prefill_workspace_size(1, 32, 8, 512, 16384, 128, 1, 7) == 0  # bad type
 
 
 def test_decode_validation(fa):
@@ -135,7 +171,7 @@ def test_decode_validation(fa):
     def call(q=A, pool=A, npages=10, pt=A, sl=A, o=A, lse=None, B=2, Hq=8, Hkv=2, Dqk=128,
              Dv=128, ps=16, maxp=4, maxlen=64, layout=fa.FA_KV_SPLIT, splits=0,
              dtype=fa.FA_BF16, ws=None, wsb=0):
-        return f(q, pool, npages, pt, sl, o, lse, B, Hq, Hkv, Dqk, Dv, ps, maxp, maxlen, layout,
+        return f(q, pool, pt, sl, npages, o, lse, B, Hq, Hkv, Dqk, Dv, ps, maxp, maxlen, layout,
                  0.1, splits, dtype, ws, wsb, stream=0)
 
     assert _err(call, pool=None) == -1

@@ -1,10 +1,10 @@
 """GPU parity of the prefill path against the CPU oracle, through the C ABI.
 
-Small shapes are compared element by element (several tiles, ragged tails,
-GQA, causal bottom-right with Sq < Skv and Sq > Skv); the full-size workloads
-(non-causal MHA 4x16x2048x64 and causal GQA 32 microbatches of 512 over 16384
-tokens) are compared on sampled rows the oracle computes one by one, in the
-launch configuration the bench times.
+Every test compares every output element (and the lse) with the oracle: small
+shapes (several tiles, ragged tails, GQA, causal bottom-right with Sq < Skv and
+Sq > Skv), and the full-size workloads -- non-causal MHA 4x16x2048x64, and
+causal GQA as 32 microbatches of 512 queries over 16384 tokens in the launch
+configuration the bench times, one test per microbatch.
 """
 import os
 
@@ -156,60 +156,65 @@ def test_causal_first_query_is_v0_exact(fa):
     np.testing.assert_array_equal(got, want)
 
 
-def test_mha_full_size_sampled(fa):
-    """Workload 2 in full (non-causal MHA B=4, 16 heads, 2048 tokens, D=64) on
-    2048 sampled rows."""
+def test_mha_full_size(fa):
+    """Workload 2 in full (non-causal MHA B=4, 16 heads, 2048 tokens, D=64):
+    every output element and every lse against the oracle."""
     inp = fi.workload(2)
     log("workload 2 full size")
     o, lse = run(fa, inp)
-    o = to_f64(o)
-    lse = to_f64(lse)
-    r = np.random.default_rng(0)
-    rows = np.stack([r.integers(0, inp.B, 2048), r.integers(0, inp.Hq, 2048),
-                     r.integers(0, inp.Sq, 2048)], axis=1)
-    ref, ref_lse = oracle.prefill_rows(inp, rows)
-    got = o[rows[:, 0], rows[:, 2], rows[:, 1]]
-    assert_parity(got, ref, "bf16", "workload 2 sampled")
-    assert_lse(lse[rows[:, 0], rows[:, 1], rows[:, 2]], ref_lse, "workload 2 sampled")
-    assert np.isfinite(o).all()
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, "bf16", "workload 2")
+    assert_lse(to_f64(lse), ref_lse, "workload 2")
 
 
-def test_gqa_ubatch_full_size_sampled(fa):
-    """Workload 3 in full: 32 microbatch calls (queries [512u, 512u+512) against
-    keys [0, 512(u+1)), causal bottom-right) with the bench's launch
-    configuration, checked on 16 sampled rows of every microbatch; the
-    concatenated output also matches one causal call over all 16384 tokens."""
+@pytest.fixture(scope="module")
+def ubatch_run(fa):
+    """Workload 3 as the bench runs it: 32 microbatch calls of fa_prefill_ex
+    (queries [512u, 512u+512) against keys [0, 512(u+1)), causal bottom-right,
+    planner-chosen waves and splits, one workspace), once without lse as the
+    bench times it and once with lse; returns (inputs, o, lse) on the host."""
     import torch
     inp = fi.workload(3)
     UB = fi.UBATCH
-    log("workload 3 full size")
     q = to_dev(inp.q, "bf16")
     k = to_dev(inp.k, "bf16")
     v = to_dev(inp.v, "bf16")
-    o = torch.empty_like(q)
-    lse = torch.empty((1, inp.Hq, inp.Sq), dtype=torch.float32, device="cuda")
     n_ub = inp.Sq // UB
-    for u in range(n_ub):
-        Skv = UB * (u + 1)
-        ws_bytes = fa.fa_prefill_workspace_size(1, inp.Hq, inp.Hkv, UB, Skv, inp.D, 1)
-        ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device="cuda")
-        fa.fa_prefill_ex(q[:, UB * u:UB * (u + 1)], k[:, :Skv], v[:, :Skv],
-                         o[:, UB * u:UB * (u + 1)], None, 1, inp.Hq, inp.Hkv, UB, Skv, inp.D, 1,
-                         inp.scale, fa.FA_BF16, fa.FA_BF16, ws, ws_bytes)
-    torch.cuda.synchronize()
-    r = np.random.default_rng(3)
-    rows = []
-    for u in range(n_ub):
-        for _ in range(16):
-            rows.append((0, int(r.integers(0, inp.Hq)), UB * u + int(r.integers(0, UB))))
-    rows = np.array(rows)
-    ref, _ = oracle.prefill_rows(inp, rows)
-    of = to_f64(o)
-    assert_parity(of[rows[:, 0], rows[:, 2], rows[:, 1]], ref, "bf16", "workload 3 sampled")
-    assert np.isfinite(of).all()
-    full, _ = fa.prefill(q, k, v, causal=True, scale=inp.scale, return_lse=True)
-    torch.cuda.synchronize()
-    assert_parity(of, to_f64(full), "bf16", "workload 3 ubatches vs one call")
+    ws_bytes = max(fa.fa_prefill_workspace_size(1, inp.Hq, inp.Hkv, UB, UB * (u + 1), inp.D, 1,
+                                                fa.FA_BF16) for u in range(n_ub))
+    ws = torch.empty(max(ws_bytes, 16) // 4 + 4, dtype=torch.float32, device="cuda")
+    outs = []
+    for with_lse in (False, True):
+        o = torch.empty_like(q)
+        lse = torch.empty((n_ub, 1, inp.Hq, UB), dtype=torch.float32, device="cuda")
+        for u in range(n_ub):
+            Skv = UB * (u + 1)
+            log(f"workload 3 microbatch {u} lse={with_lse}")
+            fa.fa_prefill_ex(q[:, UB * u:UB * (u + 1)], k[:, :Skv], v[:, :Skv],
+                             o[:, UB * u:UB * (u + 1)], lse[u] if with_lse else None, 1, inp.Hq,
+                             inp.Hkv, UB, Skv, inp.D, 1, inp.scale, fa.FA_BF16, fa.FA_BF16, ws,
+                             ws_bytes)
+        torch.cuda.synchronize()
+        outs.append((o, lse))
+    # The lse output changes no other result.
+    assert torch.equal(outs[0][0], outs[1][0])
+    return inp, to_f64(outs[0][0]), to_f64(outs[1][1])
+
+
+@pytest.mark.parametrize("u", range(32))
+def test_gqa_ubatch_full_size(ubatch_run, u):
+    """Workload 3 in full, microbatch u: all 512 x 32 output rows and their lse
+    against the oracle's causal attention over the whole 16384-token sequence
+    (rows 512u .. 512u + 511; under the bottom-right reading microbatch u
+    computes exactly those rows)."""
+    inp, o, lse = ubatch_run
+    UB = fi.UBATCH
+    rows = np.array([(0, h, i) for i in range(UB * u, UB * (u + 1)) for h in range(inp.Hq)])
+    ref, ref_lse = oracle.prefill_rows(inp, rows)
+    got = o[0, UB * u:UB * (u + 1)].reshape(-1, inp.D)  # rows in (i, h) order, as `rows`
+    assert_parity(got, ref, "bf16", f"workload 3 microbatch {u}")
+    got_lse = lse[u, 0].T.reshape(-1)  # [Hq, 512] -> (i, h) order
+    assert_lse(got_lse, ref_lse, f"workload 3 microbatch {u}")
 
 
 # --------------------------------------------------------------------------

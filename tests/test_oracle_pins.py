@@ -195,6 +195,39 @@ def test_rows_api_matches_full(oracle_lib):
         assert lrow[n] == lse[b, h, i]
 
 
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("masked", [False, True])
+def test_prefill_rows_matches_full_and_sdpa(oracle_lib, causal, masked):
+    """The row checker used for the full-size prefill workloads: on a shape where
+    B, Hq, Hkv, Sq, Skv and D all differ, every (b, h, i) row in a shuffled order
+    equals the full oracle's o[b, i, h] and lse[b, h, i] bit for bit, and torch's
+    float64 SDPA (its own gather, GQA expansion and bottom-right causal bias)
+    to 1e-12."""
+    import fa_inputs as fi
+    inp = fi.prefill_inputs(9, 3, 6, 2, 5, 11, 8, causal, "bf16")
+    if masked:
+        inp = fi.with_mask(inp, 9, "normal", batched=True, stride=16)
+    o, lse = oracle.prefill(inp)
+    rows = np.array([(b, h, i) for b in range(3) for h in range(6) for i in range(5)])
+    rows = rows[np.random.default_rng(4).permutation(len(rows))]
+    orow, lrow = oracle.prefill_rows(inp, rows)
+    np.testing.assert_array_equal(orow, o[rows[:, 0], rows[:, 2], rows[:, 1]])
+    np.testing.assert_array_equal(lrow, lse[rows[:, 0], rows[:, 1], rows[:, 2]])
+    q, k, v = (oracle.widen(x, "bf16") for x in (inp.q, inp.k, inp.v))
+    if masked:
+        m = torch.from_numpy(oracle.widen(inp.mask, "bf16")[:, None, :, :11])
+        if causal:
+            m = m + torch.where(torch.ones(5, 11, dtype=torch.bool).tril(11 - 5), 0.0,
+                                -math.inf).double()
+        tq, tk, tv = (torch.from_numpy(x).permute(0, 2, 1, 3) for x in (q, k, v))
+        ref = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=m, scale=float(inp.scale),
+                                             enable_gqa=True).permute(0, 2, 1, 3).numpy()
+    else:
+        ref = _sdpa(q, k, v, causal, float(inp.scale))
+    np.testing.assert_allclose(orow, ref[rows[:, 0], rows[:, 2], rows[:, 1]], rtol=0,
+                               atol=1e-12)
+
+
 def test_thread_count_does_not_change_result(oracle_lib):
     q, k, v = _rand(2, 9, 4, 8), _rand(2, 13, 2, 8), _rand(2, 13, 2, 8)
     o1, l1 = oracle.attention(q, k, v, True, 0.3, nthreads=1)
