@@ -23,7 +23,8 @@ __all__ = [
     "FA_BF16", "FA_FP16", "FA_FP32", "FA_KV_SPLIT", "FA_KV_MLA_SHARED", "FaError",
     "fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_prefill_workspace_size",
     "fa_decode_paged", "fa_decode_paged_multi", "fa_decode_multi_workspace_size",
-    "fa_decode_workspace_size", "fa_decode_num_splits", "fa_strerror", "fa_version",
+    "fa_decode_workspace_size", "fa_decode_num_splits", "fa_decode_paged_noalloc",
+    "fa_strerror", "fa_version",
     "prefill", "decode_paged", "LIB_PATH",
 ]
 
@@ -39,7 +40,7 @@ if not os.path.exists(LIB_PATH):
 _lib = ctypes.CDLL(LIB_PATH)
 for _name in ("fa_prefill", "fa_prefill_ex", "fa_prefill_mask", "fa_prefill_workspace_size",
               "fa_decode_paged", "fa_decode_paged_multi", "fa_decode_multi_workspace_size",
-              "fa_decode_workspace_size", "fa_decode_num_splits",
+              "fa_decode_workspace_size", "fa_decode_num_splits", "fa_decode_paged_noalloc",
               "fa_strerror", "fa_version"):
     if not hasattr(_lib, _name):
         raise ImportError(f"{LIB_PATH} lacks {_name} (older than its sources); {_BUILD_HINT}")
@@ -71,6 +72,9 @@ _lib.fa_decode_workspace_size.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
 _lib.fa_decode_workspace_size.restype = _Z
 _lib.fa_decode_num_splits.argtypes = [_I, _I, _I, _I, _I, _I, _I, _I, _I]
 _lib.fa_decode_num_splits.restype = _I
+_lib.fa_decode_paged_noalloc.argtypes = [_P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                         _I, _I, _F, _I, _I, _P]
+_lib.fa_decode_paged_noalloc.restype = _I
 _lib.fa_strerror.argtypes = [_I]
 _lib.fa_strerror.restype = ctypes.c_char_p
 _lib.fa_version.argtypes = []
@@ -175,6 +179,16 @@ def fa_decode_paged_multi(q, kv_pool, page_table, seq_lens, num_pages, o, lse, B
                                       int(layout), float(scale), int(num_splits), int(dtype),
                                       _ptr(workspace), int(workspace_bytes), _stream(stream)),
            "fa_decode_paged_multi")
+
+
+def fa_decode_paged_noalloc(q, kv_pool, page_table, seq_lens, num_pages, o, lse, B, Hq, Hkv,
+                            D_qk, D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale,
+                            num_splits, dtype, stream=None) -> None:
+    _check(_lib.fa_decode_paged_noalloc(_ptr(q), _ptr(kv_pool), _ptr(page_table),
+                                        _ptr(seq_lens), int(num_pages), _ptr(o), _ptr(lse), B,
+                                        Hq, Hkv, D_qk, D_v, page_size, max_pages_per_seq,
+                                        max_seq_len, int(layout), float(scale), int(num_splits),
+                                        int(dtype), _stream(stream)), "fa_decode_paged_noalloc")
 
 
 def fa_decode_multi_workspace_size(B, Sq, Hq, Hkv, D_qk, D_v, page_size, max_seq_len, layout,

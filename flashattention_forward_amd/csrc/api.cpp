@@ -223,6 +223,9 @@ const char* fa_strerror(int status) {
     case FA_ERR_ALIGN: return "a base pointer is not 16-byte aligned";
     case FA_ERR_WORKSPACE: return "workspace smaller than the plan needs";
     case FA_ERR_HIP: return "the HIP runtime reported an error at launch";
+    case FA_ERR_SCRATCH:
+      return "the split plan needs more than the library's static decode scratch (ask for "
+             "fewer splits)";
     default: return "unknown status";
   }
 }
@@ -501,6 +504,33 @@ int fa_decode_paged_multi(const void* q, const void* kv_pool, const int32_t* pag
   return decode_impl(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Sq, Hq, Hkv, D_qk,
                      D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale, num_splits,
                      dtype, workspace, workspace_bytes, stream);
+}
+
+int fa_decode_paged_noalloc(const void* q, const void* kv_pool, const int32_t* page_table,
+                            const int32_t* seq_lens, int num_pages, void* o, float* lse, int B,
+                            int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                            int max_pages_per_seq, int max_seq_len, fa_kv_layout layout,
+                            float scale, int num_splits, fa_dtype dtype, hipStream_t stream) {
+  // The plan (and so the result) is the one fa_decode_paged makes with a
+  // workspace; its partials must fit the static scratch. Everything is
+  // checked on the host before the scratch is looked up or anything enqueued.
+  int rc = check_decode(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, Hq, Hkv, D_qk,
+                        D_v, page_size, max_pages_per_seq, max_seq_len, layout, dtype);
+  if (rc != FA_OK) return rc;
+  if (B == 0) return FA_OK;
+  const DecodePlan pl = plan_decode(B, Hq, Hkv, D_v, max_seq_len, layout, num_splits, true);
+  if (pl.ws_bytes > NOALLOC_SCRATCH_BYTES) return FA_ERR_SCRATCH;
+  // The scratch is passed even when the plan does not split, so that the
+  // call plans exactly as above.
+  void* ws = nullptr;
+  if (device_scratch(&ws) != hipSuccess) {
+    (void)hipGetLastError();
+    return FA_ERR_HIP;
+  }
+  return decode_impl(q, kv_pool, num_pages, page_table, seq_lens, o, lse, B, 1, Hq, Hkv, D_qk,
+                     D_v, page_size, max_pages_per_seq, max_seq_len, layout, scale, num_splits,
+                     dtype, ws, NOALLOC_SCRATCH_BYTES, stream);
+  static_assert(NOALLOC_SCRATCH_BYTES == FA_DECODE_NOALLOC_SCRATCH_BYTES, "scratch size");
 }
 
 size_t fa_decode_multi_workspace_size(int B, int Sq, int Hq, int Hkv, int D_qk, int D_v,

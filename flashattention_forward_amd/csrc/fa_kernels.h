@@ -91,6 +91,11 @@ hipError_t launch_prefill_pp(const PrefillParams& p, InType it, OutType ot, bool
 hipError_t launch_decode_mla(const DecodeMlaParams& p, InType it, hipStream_t stream);
 hipError_t launch_combine(const CombineParams& p, OutType ot, hipStream_t stream);
 
+// Device address (for the current device) of the library's static split-KV
+// scratch of NOALLOC_SCRATCH_BYTES, looked up once per device; allocates nothing.
+constexpr size_t NOALLOC_SCRATCH_BYTES = (size_t)32 << 20;  // FA_DECODE_NOALLOC_SCRATCH_BYTES
+hipError_t device_scratch(void** ptr);
+
 // Tile constants the host planner needs.
 // Prefill: each wave owns 32 query rows; a workgroup has 4 or 8 waves (128 or
 // 256 query rows). With 8 waves (head size 128, one workgroup per CU) every

@@ -66,7 +66,8 @@ enum {
   FA_ERR_UNSUPPORTED = -3, /* head size / dtype combination not built */
   FA_ERR_ALIGN = -4,       /* a base pointer is not 16-byte aligned */
   FA_ERR_WORKSPACE = -5,   /* workspace smaller than the plan needs */
-  FA_ERR_HIP = -6          /* the HIP runtime reported an error at launch */
+  FA_ERR_HIP = -6,         /* the HIP runtime reported an error at launch */
+  FA_ERR_SCRATCH = -7      /* a no-alloc call's split plan exceeds the static scratch */
 };
 
 /*
@@ -240,6 +241,29 @@ size_t fa_decode_workspace_size(int B, int Hq, int Hkv, int D_qk, int D_v, int p
  * the compute units of the current device (FA_NUM_CUS overrides them). */
 int fa_decode_num_splits(int B, int Hq, int Hkv, int D_qk, int D_v, int page_size,
                          int max_seq_len, fa_kv_layout layout, int num_splits);
+
+/*
+ * Paged decode that allocates nothing and takes no workspace, for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight serving
+ * loops, harnesses that forbid hipMalloc. Same arguments, plan, kernels and
+ * results as fa_decode_paged with a workspace, except that the split-KV
+ * partials go to a static device buffer the library owns: 32 MiB per GPU
+ * (FA_DECODE_NOALLOC_SCRATCH_BYTES), held until the process ends. A plan whose
+ * partials (splits x B x Hq x (2 D_v + 4) bytes) exceed it fails with
+ * FA_ERR_SCRATCH before anything is enqueued; num_splits can then ask for
+ * fewer. The call makes no hipMalloc / hipFree and no allocating library call;
+ * its first call on a device looks up that device's copy of the buffer.
+ * Every call on one GPU shares the buffer: calls that overlap on one GPU (on
+ * different streams without ordering) race on it; calls ordered on one stream
+ * do not. Errors: those of fa_decode_paged (without FA_ERR_WORKSPACE), plus
+ * FA_ERR_SCRATCH, and FA_ERR_HIP if the buffer's address cannot be looked up.
+ */
+#define FA_DECODE_NOALLOC_SCRATCH_BYTES ((size_t)32 << 20)
+int fa_decode_paged_noalloc(const void* q, const void* kv_pool, const int32_t* page_table,
+                            const int32_t* seq_lens, int num_pages, void* o, float* lse, int B,
+                            int Hq, int Hkv, int D_qk, int D_v, int page_size,
+                            int max_pages_per_seq, int max_seq_len, fa_kv_layout layout,
+                            float scale, int num_splits, fa_dtype dtype, hipStream_t stream);
 
 /* Static text for a status code. */
 const char* fa_strerror(int status);

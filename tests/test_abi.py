@@ -220,6 +220,23 @@ def test_decode_split_planning(fa, monkeypatch):
     assert fa.fa_decode_workspace_size(4, 32, 8, 128, 128, 16, 100, fa.FA_KV_SPLIT, 1) == 0
 
 
+def test_decode_noalloc_validation(fa):
+    """The entry point that allocates nothing checks its arguments like
+    fa_decode_paged, and refuses a split plan larger than its static scratch
+    before touching the device."""
+    def call(B=2, splits=0, maxlen=64, layout=fa.FA_KV_SPLIT, Dqk=128, Dv=128, pool=A):
+        return fa.fa_decode_paged_noalloc(A, pool, A, A, 10, A, None, B, 8, 2 if Dqk == 128 else 1,
+                                          Dqk, Dv, 1, maxlen, maxlen, layout, 0.1, splits,
+                                          fa.FA_BF16, stream=0)
+    assert _err(call, pool=None) == -1
+    assert _err(call, Dqk=64, Dv=64) == -3
+    mla = fa.FA_KV_MLA_SHARED
+    # 2048 sequences x 8 heads x 16 splits of 512-column partials: 136 MB > 32 MiB
+    assert _err(call, B=2048, splits=16, maxlen=8192, layout=mla, Dqk=576, Dv=512) == -7
+    assert "scratch" in fa.fa_strerror(-7)
+    call(B=0)  # empty batch: nothing enqueued
+
+
 def test_binding_rejects_host_tensors(fa):
     import torch
     x = torch.zeros(16, dtype=torch.bfloat16)
