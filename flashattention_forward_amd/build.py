@@ -20,8 +20,8 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libfa.so")
 
-SOURCES = ["prefill.hip", "prefill_pp.hip", "decode.hip", "decode_mla.hip", "combine.hip",
-           "noalloc.hip", "api.cpp"]
+SOURCES = ["prefill.hip", "prefill_f16.hip", "prefill_d64.hip", "prefill_pp.hip", "decode.hip",
+           "decode_mla.hip", "combine.hip", "noalloc.hip", "api.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -71,6 +71,7 @@ constexpr int64_t kMaxGrid = 0x7fffffff;
 // ---------------------------------------------------------------------------
 struct PrefillPlan {
   int waves = 4;
+  int pack = 1;  // query heads per workgroup
   int n_qtiles = 0;
   int n_splits = 1;
   size_t ws_bytes = 0;
@@ -88,7 +89,7 @@ int prefill_splits(int64_t base, int max_tiles, int waves) {
 
 // out_bytes: bytes per element of the output type, which the split partials
 // share (2 for bf16/fp16, 4 for fp32).
-PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split,
+PrefillPlan plan_prefill(int B, int Hq, int Hkv, int Sq, int Skv, int D, bool allow_split,
                          int out_bytes) {
   PrefillPlan pl;
   const int max_tiles = ceil_div(Skv, PF_BN);
@@ -103,8 +104,29 @@ PrefillPlan plan_prefill(int B, int Hq, int Sq, int Skv, int D, bool allow_split
   const int forced_w = env_int("FA_PREFILL_WAVES", 0);
   if (D == 128 && (forced_w == 4 || forced_w == 8)) waves = forced_w;
   pl.waves = waves;
-  pl.n_qtiles = ceil_div(Sq, 32 * waves);
-  const int64_t base = (int64_t)B * Hq * pl.n_qtiles;
+  // Head packs (the grouped-query packing of the same llama.cpp paragraph): a
+  // workgroup takes PK query heads of one K/V head over 32 waves / PK rows, so
+  // each K/V and mask tile it copies serves PK heads, and the causal diagonal
+  // costs fewer masked tiles per workgroup. PK is the largest power of two
+  // that divides the group size and the waves (workload 3 as 32 microbatches:
+  // 2547 us unpacked, 2385 / 2412 us with packs of 2 / 4; with a distance-bias
+  // mask 3259 / 2869 / 2801 us). FA_PREFILL_PACK forces a pack (1 = one head).
+  const int G = Hq / Hkv;
+  int pack = 1;
+  for (int pk = waves; pk > 1; pk /= 2)
+    if (G % pk == 0) {
+      pack = pk;
+      break;
+    }
+  const int forced_pk = env_int("FA_PREFILL_PACK", 0);
+  if (forced_pk >= 1 && forced_pk <= waves && waves % forced_pk == 0 && G % forced_pk == 0)
+    pack = forced_pk;
+  if (waves == 8 && env_int("FA_PREFILL_PINGPONG", 0) != 0) pack = 1;  // one-head tiling only
+  pl.pack = pack;
+  pl.n_qtiles = ceil_div(Sq, 32 * waves / pack);
+  // Splits are planned from the one-head tiling, so the workspace a shape needs
+  // does not depend on the pack (nor on whether the call has a mask).
+  const int64_t base = (int64_t)B * Hq * ceil_div(Sq, 32 * waves);
   int S = 1;
   if (allow_split && base > 0) {
     const int forced = env_int("FA_PREFILL_SPLITS", 0);
@@ -236,7 +258,8 @@ size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D,
   (void)causal;
   if (B < 1 || Hq < 1 || Sq < 1 || Skv < 0 || (D != 64 && D != 128)) return 0;
   if (out_dtype != FA_BF16 && out_dtype != FA_FP16 && out_dtype != FA_FP32) return 0;
-  return plan_prefill(B, Hq, Sq, Skv, D, true, out_dtype == FA_FP32 ? 4 : 2).ws_bytes;
+  if (Hkv < 1 || Hq % Hkv != 0) return 0;
+  return plan_prefill(B, Hq, Hkv, Sq, Skv, D, true, out_dtype == FA_FP32 ? 4 : 2).ws_bytes;
 }
 
 static int prefill_impl(const void* q, const void* k, const void* v, const void* mask,
@@ -249,9 +272,10 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
   if (workspace && !aligned16(workspace)) return FA_ERR_ALIGN;
   if (Sq == 0) return FA_OK;
   const int out_bytes = out_dtype == FA_FP32 ? 4 : 2;
-  const PrefillPlan pl = plan_prefill(B, Hq, Sq, Skv, D, workspace != nullptr, out_bytes);
+  const PrefillPlan pl =
+      plan_prefill(B, Hq, Hkv, Sq, Skv, D, workspace != nullptr, out_bytes);
   if (pl.ws_bytes > 0 && workspace_bytes < pl.ws_bytes) return FA_ERR_WORKSPACE;
-  if ((int64_t)B * Hq * pl.n_qtiles * pl.n_splits > kMaxGrid) return FA_ERR_SHAPE;
+  if ((int64_t)B * (Hq / pl.pack) * pl.n_qtiles * pl.n_splits > kMaxGrid) return FA_ERR_SHAPE;
   if (pl.n_splits > 1 && (int64_t)B * Sq * Hq > INT_MAX) return FA_ERR_SHAPE;
 
   PrefillParams p{};
@@ -266,6 +290,7 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
   p.Sq = Sq;
   p.Skv = Skv;
   p.waves = pl.waves;
+  p.pack = pl.pack;
   p.pingpong = env_int("FA_PREFILL_PINGPONG", 0) != 0;
   p.n_qtiles = pl.n_qtiles;
   p.n_splits = pl.n_splits;

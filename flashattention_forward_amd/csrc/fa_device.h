@@ -14,6 +14,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace fa {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -210,6 +212,16 @@ __device__ __forceinline__ u32x4 neg16x8(u32x4 v) {
 __device__ __forceinline__ int blk_slot(int r, int c) {
   const int g = c & 7;
   return 8 * (g ^ ((r >> 3) & 1)) + ((r & 7) ^ (4 * ((g >> 1) & 1)));
+}
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = B .. E - 1, each
+// a separate instantiation, so indices into register arrays stay constants
+// without relying on the loop unroller.
+template <int B, int E, typename F> __device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
 }
 
 // Online-softmax rescale threshold in log2 units: the running max is moved

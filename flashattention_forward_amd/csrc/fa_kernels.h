@@ -21,8 +21,9 @@ struct PrefillParams {
   float* part_lse;  // [S, B, Sq, Hq]
   int B, Hq, Hkv, Sq, Skv;
   int waves;     // waves per workgroup: 4 or 8 (8 only for head size 128)
+  int pack;      // query heads per workgroup (1, 2, 4 or 8; divides Hq / Hkv and waves)
   int pingpong;  // 8 waves: the two-group ping-pong schedule (prefill_pp.hip)
-  int n_qtiles;  // ceil(Sq / (32 * waves))
+  int n_qtiles;  // ceil(Sq / (32 * waves / pack))
   int n_splits;  // key splits per query tile
   int q_neg;     // 1: the scale was negative; the kernel uses -Q and |scale|
   float scale;       // |scale|, multiplies q.k
@@ -85,6 +86,15 @@ struct CombineParams {
 
 hipError_t launch_prefill(const PrefillParams& p, int D, InType it, OutType ot, bool causal,
                           hipStream_t stream);
+// Per (head size, input type) prefill launchers, each compiled in its own file.
+hipError_t launch_prefill_128_bf16(const PrefillParams& p, OutType ot, bool causal,
+                                   hipStream_t stream);
+hipError_t launch_prefill_128_f16(const PrefillParams& p, OutType ot, bool causal,
+                                  hipStream_t stream);
+hipError_t launch_prefill_64_bf16(const PrefillParams& p, OutType ot, bool causal,
+                                  hipStream_t stream);
+hipError_t launch_prefill_64_f16(const PrefillParams& p, OutType ot, bool causal,
+                                 hipStream_t stream);
 hipError_t launch_decode_split(const DecodeSplitParams& p, InType it, hipStream_t stream);
 hipError_t launch_prefill_pp(const PrefillParams& p, InType it, OutType ot, bool causal,
                              hipStream_t stream);

@@ -310,3 +310,46 @@ def test_prefill_zero_mask_equals_unmasked(fa):
     o1 = fa.prefill(q, k, v, causal=True, scale=inp.scale, mask=zero)
     torch.cuda.synchronize()
     assert_parity(to_f64(o1), to_f64(o0).astype(np.float64), "bf16", "zero mask vs none")
+
+
+# --------------------------------------------------------------------------
+# head packs: a workgroup takes PK query heads of one K/V head
+# --------------------------------------------------------------------------
+
+PACK_SHAPES = [
+    # B, Hq, Hkv, Sq, Skv, D, causal, in, out
+    (1, 8, 2, 200, 333, 128, True, "bf16", "bf16"),     # G = 4, ragged
+    (2, 16, 2, 130, 700, 128, False, "bf16", "bf16"),   # G = 8
+    (1, 6, 3, 129, 400, 64, True, "fp16", "fp32"),      # G = 2, head size 64
+    (1, 32, 8, 512, 1536, 128, True, "bf16", "bf16"),   # a workload-3 microbatch
+    (1, 4, 1, 40, 30, 128, True, "bf16", "bf16"),       # Sq > Skv: leading rows see nothing
+]
+
+
+@pytest.mark.parametrize("masked", [False, True], ids=["nomask", "mask"])
+@pytest.mark.parametrize("splits", ["auto", "3"])
+@pytest.mark.parametrize("pack", ["1", "2", "4", "8"])
+@pytest.mark.parametrize("waves", ["4", "8"])
+@pytest.mark.parametrize("shape", PACK_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_head_pack(fa, shape, waves, pack, splits, masked, monkeypatch):
+    """Every head pack the shape allows (PK query heads of one K/V head per
+    workgroup, the mask tile copied once for them into a shared ring), with
+    and without an additive mask, both workgroup shapes and split counts, gives
+    the oracle's result. A pack the shape does not allow falls back to the
+    planner's."""
+    monkeypatch.setenv("FA_PREFILL_WAVES", waves)
+    monkeypatch.setenv("FA_PREFILL_PACK", pack)
+    if splits != "auto":
+        monkeypatch.setenv("FA_PREFILL_SPLITS", splits)
+    B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
+    log(f"prefill pack={pack} waves={waves} splits={splits} mask={masked} {shape}")
+    if masked:
+        inp = _mask_inputs(64, shape, "bias", pad=8)
+        o, lse = run_masked(fa, inp)
+    else:
+        inp = fi.prefill_inputs(64, *shape)
+        o, lse = run(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    what = f"pack={pack} waves={waves} splits={splits} mask={masked} {shape}"
+    assert_parity(to_f64(o), ref, it, what)
+    assert_lse(to_f64(lse), ref_lse, what, dtype=it)
