@@ -357,7 +357,7 @@ def main():
     pf_tflops = flops3 * K / t_pf / 1e12
     dec_gbs = bytes4 * K / t_dec / 1e9
 
-    sha_pf = source_sha("prefill.hip", "combine.hip", "fa_device.h")
+    sha_pf = source_sha("prefill_kernel.h", "prefill.hip", "combine.hip", "fa_device.h")
     sha_dec = source_sha("decode_mla.hip", "combine.hip", "fa_device.h")
     tr_pf, tr_pf_launch = traffic_for("prefill", sha_pf) or (None, None)
     tr_dec, tr_dec_launch = traffic_for("decode_mla", sha_dec) or (None, None)
