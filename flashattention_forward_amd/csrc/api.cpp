@@ -11,6 +11,7 @@
 #include <climits>
 #include <cmath>
 #include <cstdint>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 
@@ -57,6 +58,13 @@ int env_int(const char* name, int dflt) {
   const char* e = std::getenv(name);
   if (!e || !*e) return dflt;
   return std::atoi(e);
+}
+
+// FA_LOG=1 prints, per call, the plan it launches (one line on stderr). The
+// variable is read once per process.
+bool log_plans() {
+  static const bool on = env_int("FA_LOG", 0) != 0;
+  return on;
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -311,6 +319,13 @@ static int prefill_impl(const void* q, const void* k, const void* v, const void*
   const OutType ot = out_dtype == FA_BF16 ? OutType::bf16
                      : out_dtype == FA_FP16 ? OutType::f16
                                             : OutType::f32;
+  if (log_plans())
+    std::fprintf(stderr,
+                 "fa_log prefill B=%d Hq=%d Hkv=%d Sq=%d Skv=%d D=%d causal=%d mask=%d "
+                 "cus=%d waves=%d pack=%d qtiles=%d splits=%d workgroups=%lld ws_bytes=%zu\n",
+                 B, Hq, Hkv, Sq, Skv, D, causal != 0, mask != nullptr, planner_cus(), pl.waves,
+                 pl.pack, pl.n_qtiles, pl.n_splits,
+                 (long long)B * (Hq / pl.pack) * pl.n_qtiles * pl.n_splits, pl.ws_bytes);
   if (launch_prefill(p, D, it, ot, causal != 0, stream) != hipSuccess) return FA_ERR_HIP;
   if (pl.n_splits > 1) {
     CombineParams c{};
@@ -435,6 +450,13 @@ static int decode_impl(const void* q, const void* kv_pool, int num_pages,
     part_lse = (float*)((char*)workspace + (size_t)pl.n_splits * rows * D_v * 2);
   }
   const InType it = dtype == FA_BF16 ? InType::bf16 : InType::f16;
+  if (log_plans())
+    std::fprintf(stderr,
+                 "fa_log decode layout=%s B=%d Sq=%d Hq=%d Hkv=%d page_size=%d max_seq_len=%d "
+                 "cus=%d splits=%d chunk=%d row_blocks=%d heads_per_wg=%d ws_bytes=%zu\n",
+                 layout == FA_KV_MLA_SHARED ? "mla" : "split", B, Sq, Hq, Hkv, page_size,
+                 max_seq_len, planner_cus(), pl.n_splits, pl.chunk, pl.n_hblk,
+                 layout == FA_KV_MLA_SHARED ? pl.heads_per_wg : 0, pl.ws_bytes);
   hipError_t e;
   if (layout == FA_KV_MLA_SHARED) {
     DecodeMlaParams p{};

@@ -347,6 +347,7 @@ __global__ __launch_bounds__(MLA_THREADS, 2) void decode_mla_kernel(DecodeMlaPar
     pg[d] = pt_load(s + 2 * INFL);
     lds_barrier();
     compute(s);
+    debug_step_barrier();
   };
   for (int s = 0; s < n_steps; s += INFL) {
 #pragma unroll

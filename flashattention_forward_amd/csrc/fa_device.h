@@ -122,24 +122,57 @@ __device__ __forceinline__ int xcd_remap(int pid, int n) {
   return x < r ? x * (q + 1) + s : r * (q + 1) + (x - r) * q + s;
 }
 
+// LDS-race debug build (compiled with -DFA_LDS_DEBUG=1 into a library of its
+// own): every LDS hand-off below also waits for all of the wave's
+// vector-memory operations (global-to-LDS copies included), every partial
+// vmcnt wait waits for all of them, and the loops over the workgroup-shared
+// K/V stages end each step with a full barrier (debug_step_barrier). The
+// arithmetic and its order are unchanged, so the debug library's results must
+// equal the fast build's bit for bit; a difference means a stage was read
+// before its copy landed or overwritten while another wave still read it.
+#ifndef FA_LDS_DEBUG
+#define FA_LDS_DEBUG 0
+#endif
+
 // Wave-local ordering of LDS accesses (all lanes' earlier LDS ops completed
 // before later ones are issued; also a compiler barrier).
 __device__ __forceinline__ void wave_lds_sync() {
+#if FA_LDS_DEBUG
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)" ::: "memory");
+#else
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#endif
 }
 
 // Workgroup barrier for LDS traffic only: this wave's LDS operations are
 // complete, then all waves meet. Unlike __syncthreads() it does not wait for
 // outstanding global loads, so prefetches stay in flight across it.
 __device__ __forceinline__ void lds_barrier() {
+#if FA_LDS_DEBUG
+  asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#else
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+#endif
+}
+
+// End of one step of a loop over workgroup-shared LDS stages: a full barrier
+// in the debug build, nothing otherwise. Only for places that every wave of
+// the workgroup reaches equally often (beside an lds_barrier of the same loop).
+__device__ __forceinline__ void debug_step_barrier() {
+#if FA_LDS_DEBUG
+  lds_barrier();
+#endif
 }
 
 // Wait until at most N of this wave's vector-memory operations are
 // outstanding (they retire in issue order).
 template <int N> __device__ __forceinline__ void wait_vmcnt() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
+#if FA_LDS_DEBUG
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#else
   asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+#endif
 }
 
 // LDS byte address (offset in the workgroup's LDS) of a __shared__ pointer.

@@ -1,8 +1,10 @@
 // Kernel parameter blocks and host-side launch wrappers of the gfx950 kernels.
-// Shared by the kernel sources and the C-ABI front end (api.cpp).
+// Shared by the kernel sources and the C-ABI front end (api.cpp). Host-only
+// declarations: the front end also builds with a plain C++ compiler (the
+// sanitizer build of the host logic), so only the runtime API header is used.
 #pragma once
 
-#include <hip/hip_runtime.h>
+#include <hip/hip_runtime_api.h>
 #include <stdint.h>
 
 namespace fa {

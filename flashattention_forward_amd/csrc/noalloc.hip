@@ -12,6 +12,8 @@
 // call's contents in it; the decode kernels write every partial row and lse
 // they read back, so nothing has to start at zero. Calls that overlap on one
 // GPU (different streams, no ordering) race on it.
+#include <hip/hip_runtime.h>
+
 #include <atomic>
 #include <mutex>
 

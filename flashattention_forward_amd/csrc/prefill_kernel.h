@@ -555,6 +555,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
            mread + m_stage(t + 1));
     else
       body(cur, nxt, smem + k_stage(t + 1), smem + v_stage(t), nb, mx_pend, kNow, nullptr);
+    debug_step_barrier();
   };
   constexpr std::integral_constant<bool, false> kFull{};
   constexpr std::integral_constant<bool, true> kMasked{};

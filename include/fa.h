@@ -36,6 +36,10 @@
  *    sequence lengths: 4-byte aligned).
  *  - Calls on one stream are ordered; calls that share a workspace must not
  *    run concurrently on different streams.
+ *  - With the environment variable FA_LOG=1 (read once per process) every
+ *    compute call that passes validation prints the plan it launches (compute
+ *    units planned for, workgroup shape, head pack, key splits, workspace
+ *    bytes) as one "fa_log ..." line on stderr.
  */
 #ifndef FA_H
 #define FA_H

@@ -62,10 +62,15 @@ def test_binding_argument_counts(fa):
         assert len(fn.argtypes) == n, f"{name}: binding {len(fn.argtypes)} vs header {n}"
 
 
-def test_library_exports_every_declared_symbol(fa):
-    lib = ctypes.CDLL(fa.LIB_PATH)
+@pytest.mark.parametrize("lib_name", ["libfa.so", "libfa_ldsdebug.so"])
+def test_library_exports_every_declared_symbol(fa, lib_name):
+    """Both builds (the library and its LDS-race debug build) load and export
+    every function fa.h declares."""
+    path = os.path.join(os.path.dirname(fa.LIB_PATH), lib_name)
+    assert os.path.exists(path), f"{path} is not built"
+    lib = ctypes.CDLL(path)
     for n in declared_functions():
-        assert hasattr(lib, n), f"{n} declared in fa.h but not exported"
+        assert hasattr(lib, n), f"{n} declared in fa.h but not exported by {lib_name}"
 
 
 def test_strerror_and_version(fa):
