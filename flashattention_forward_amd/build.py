@@ -35,10 +35,14 @@ SOURCES = ["prefill.hip", "prefill_f16.hip", "prefill_d64.hip", "prefill_pp.hip"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 # No fast-math: -inf scores and exp2(-inf) = 0 must stay IEEE. Packed fp32 VALU
-# forms are switched off for all device code.
+# forms are switched off for all device code. MFMA accumulators stay in
+# ordinary VGPRs (-amdgpu-mfma-vgpr-form): left to its heuristics the compiler
+# put the paged GQA decode's accumulators in AGPRs and copied all of them to
+# VGPRs and back on every tile (about 70 extra instructions per tile); the
+# other kernels already get the VGPR form.
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Wall",
          "-Wno-unused-result", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
-         f"-I{INCLUDE}", f"-I{CSRC}"]
+         "-mllvm", "-amdgpu-mfma-vgpr-form=1", f"-I{INCLUDE}", f"-I{CSRC}"]
 
 
 def _compile(job) -> str:

@@ -388,6 +388,9 @@ static int check_decode(const void* q, const void* kv_pool, int num_pages,
   if ((int64_t)max_pages_per_seq * page_size < max_seq_len) return FA_ERR_SHAPE;
   if (layout == FA_KV_SPLIT) {
     if (D_qk != 128 || D_v != 128) return FA_ERR_UNSUPPORTED;
+    // The kernel addresses a page's bytes (K and V blocks of every K/V head)
+    // with 32-bit offsets.
+    if ((int64_t)2 * Hkv * page_size * D_qk * 2 > INT32_MAX) return FA_ERR_SHAPE;
   } else if (layout == FA_KV_MLA_SHARED) {
     if (D_qk != 576 || D_v != 512) return FA_ERR_UNSUPPORTED;
     if (Hkv != 1) return FA_ERR_SHAPE;

@@ -30,17 +30,6 @@
 
 namespace fa {
 
-template <int PS>
-__device__ __forceinline__ void page_of(int key, int ps, int& page_idx, int& slot) {
-  if (PS > 0) {
-    page_idx = key / PS;
-    slot = key % PS;
-  } else {
-    page_idx = key / ps;
-    slot = key - page_idx * ps;
-  }
-}
-
 // ---------------------------------------------------------------------------
 // Grouped-query decode over the split K/V pool [P, 2, Hkv, page, 128].
 // One wave is one work unit (sequence b, K/V head g, block of up to 16 query
@@ -85,61 +74,86 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
 #pragma unroll
     for (int s = 0; s < D / 32; ++s)
       qf[s] = hvalid ? ldg16(qrow + (32 * s + 8 * gq) * 2) : u32x4{0, 0, 0, 0};
-#pragma unroll
-    for (int s = 0; s < D / 32; ++s)
-      if (p.q_neg) qf[s] = neg16x8(qf[s]);
   }
   const int32_t* ptab = p.page_table + (int64_t)b * p.max_pages;
-  const int64_t page_stride = (int64_t)2 * p.Hkv * p.page_size * D * 2;  // bytes per page
-  const int64_t kv_stride = (int64_t)p.Hkv * p.page_size * D * 2;       // K -> V bytes
+  // Bytes per page and from a page's K block to its V block (a page is below
+  // 2 GiB: checked on the host).
+  const unsigned page_stride = 2u * (unsigned)p.Hkv * (unsigned)p.page_size * D * 2;
+  const unsigned kv_stride = (unsigned)p.Hkv * (unsigned)p.page_size * D * 2;
   const char* pool_g = (const char*)p.pool + (int64_t)g * p.page_size * D * 2;
 
   // Each lane touches 10 token rows of a 32-token tile: 2 as key rows of the
   // MFMA A operand (tokens 16*kb + c16) and 8 as value rows copied to LDS
-  // (tokens gq + 4*r). Their page ids are fetched two tiles ahead, so no data
-  // load waits on a page-table load. Invalid tokens (past the split or with an
-  // out-of-range page id) load pool row 0 and are zeroed by a select.
-  auto fetch_pages = [&](int (&pg)[10], int tt) {
+  // (tokens gq + 4*r). With a page size that is a multiple of 16 every 16-token
+  // half of a tile lies in one page, so a lane needs the page ids of the two
+  // halves only (HALVES); otherwise it needs one per row. The ids are fetched
+  // two tiles ahead, so no row load waits on a page-table load; the table is
+  // read at a clamped (valid) index and the id replaced by -1 past the split's
+  // end, with no branch. Invalid rows (past the split, or with an out-of-range
+  // page id) load the pool's first row and are zeroed by a select. Key and
+  // slot arithmetic is unsigned (keys are never negative), and a page's bytes
+  // fit in 32 bits (checked on the host), so a row's offset is one 32 x 32 ->
+  // 64-bit multiply-add.
+  constexpr bool HALVES = PS > 0 && PS % 16 == 0;
+  constexpr int NPG = HALVES ? 2 : 10;
+  const unsigned last_key = (unsigned)max(t1 - 1, 0);
+  const unsigned psize = PS > 0 ? (unsigned)PS : (unsigned)p.page_size;
+  auto row_key = [&](int r, int tt) { return tt + (r < 2 ? 16 * r + c16 : gq + 4 * (r - 2)); };
+  auto fetch_pages = [&](int (&pg)[NPG], int tt) {
 #pragma unroll
-    for (int r = 0; r < 10; ++r) {
-      const int key = tt + (r < 2 ? 16 * r + c16 : gq + 4 * (r - 2));
-      int pi, slot;
-      page_of<PS>(min(key, max(t1 - 1, 0)), p.page_size, pi, slot);
-      pg[r] = key < t1 ? ptab[pi] : -1;
+    for (int i = 0; i < NPG; ++i) {
+      const int key = HALVES ? tt + 16 * i : row_key(i, tt);
+      const unsigned kc = min((unsigned)key, last_key);
+      const int id = ptab[kc / psize];
+      pg[i] = key < t1 ? id : -1;
     }
   };
-  auto row_off = [&](const int (&pg)[10], int r, int tt, bool& ok) -> int64_t {
-    const int key = tt + (r < 2 ? 16 * r + c16 : gq + 4 * (r - 2));
-    int pi, slot;
-    page_of<PS>(key, p.page_size, pi, slot);
-    ok = (unsigned)pg[r] < (unsigned)p.num_pages;
-    return ok ? (int64_t)pg[r] * page_stride + (int64_t)slot * D * 2 : 0;
+  auto row_off = [&](const int (&pg)[NPG], int r, int tt, bool& ok) -> uint64_t {
+    const int key = row_key(r, tt);
+    const int id = HALVES ? pg[r < 2 ? r : (r - 2) / 4] : pg[r];
+    const unsigned slot = (unsigned)key % psize;
+    ok = key < t1 && (unsigned)id < (unsigned)p.num_pages;
+    const uint64_t o = (uint64_t)(unsigned)id * page_stride + slot * (unsigned)(D * 2);
+    return ok ? o : 0;
   };
 
   // One tile in flight: K of tile t + 1 is loaded into the registers that K
   // of tile t has just fed to the score MFMAs, and V of tile t + 1 into the
-  // staging registers once V of tile t is in LDS.
+  // staging registers once V of tile t is in LDS. (Two tiles in flight, with
+  // the loads issued on every path, measured no faster on the small-batch
+  // workload, 50.5 against 47.7 us: the waves are not waiting on a single
+  // tile's latency.)
   u32x4 kr[2][D / 32], vr[8];
   bool kok[2], vok[8];
-  auto load_k = [&](const int (&pg)[10], int tt) {
+  auto load_k = [&](const int (&pg)[NPG], int tt) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int64_t o = row_off(pg, kb, tt, kok[kb]);
+      const uint64_t o = row_off(pg, kb, tt, kok[kb]);
 #pragma unroll
       for (int s = 0; s < D / 32; ++s) kr[kb][s] = ldg16(pool_g + o + (32 * s + 8 * gq) * 2);
     }
   };
-  auto load_v = [&](const int (&pg)[10], int tt) {
+  auto load_v = [&](const int (&pg)[NPG], int tt) {
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-      const int64_t o = row_off(pg, 2 + r, tt, vok[r]);
+      const uint64_t o = row_off(pg, 2 + r, tt, vok[r]);
       vr[r] = ldg16(pool_g + o + kv_stride + c16 * 16);
     }
   };
+  // Rows outside the split (or with a page id out of range) are zeroed only
+  // in a tile that has one: the last tile of a split.
   auto store_v = [&]() {
+    bool all = true;
 #pragma unroll
-    for (int r = 0; r < 8; ++r)
-      *(u32x4*)(vlds + ((gq + 4 * r) * DS_VS + c16 * 8) * 2) = vok[r] ? vr[r] : u32x4{0, 0, 0, 0};
+    for (int r = 0; r < 8; ++r) all = all && vok[r];
+    if (__ballot(!all)) {
+#pragma unroll
+      for (int r = 0; r < 8; ++r)
+        *(u32x4*)(vlds + ((gq + 4 * r) * DS_VS + c16 * 8) * 2) = vok[r] ? vr[r] : u32x4{0, 0, 0, 0};
+    } else {
+#pragma unroll
+      for (int r = 0; r < 8; ++r) *(u32x4*)(vlds + ((gq + 4 * r) * DS_VS + c16 * 8) * 2) = vr[r];
+    }
   };
 
   f32x4 oacc[D / 16];
@@ -149,23 +163,34 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
   const float sl2 = p.scale_log2;
 
   // pg holds the page ids of the tile whose loads are issued next.
-  int pg[10];
+  int pg[NPG];
   if (t0 < t1) {
     fetch_pages(pg, t0);
     load_k(pg, t0);
     load_v(pg, t0);
     fetch_pages(pg, t0 + DEC_TILE);
   }
+  // A negative scale runs as -Q with |scale|; the sign is applied after the
+  // first tile's loads are issued, so the query loads overlap the page-table
+  // and row loads instead of being waited for first.
+  if (p.q_neg) {
+#pragma unroll
+    for (int s = 0; s < D / 32; ++s) qf[s] = neg16x8(qf[s]);
+  }
   for (int tt = t0; tt < t1; tt += DEC_TILE) {
     const bool more = tt + DEC_TILE < t1;
     f32x4 sacc[2] = {f32x4{}, f32x4{}};
+    if (__ballot(!(kok[0] && kok[1]))) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int s = 0; s < D / 32; ++s)
+          if (!kok[kb]) kr[kb][s] = u32x4{0, 0, 0, 0};
+    }
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
 #pragma unroll
-      for (int s = 0; s < D / 32; ++s) {
-        const u32x4 kv = kok[kb] ? kr[kb][s] : u32x4{0, 0, 0, 0};
-        sacc[kb] = T::mma16(kv, qf[s], sacc[kb]);
-      }
+      for (int s = 0; s < D / 32; ++s) sacc[kb] = T::mma16(kr[kb][s], qf[s], sacc[kb]);
     }
     if (more) load_k(pg, tt + DEC_TILE);
     wave_lds_sync();  // the previous tile's V reads are done

@@ -180,7 +180,9 @@ size_t fa_prefill_workspace_size(int B, int Hq, int Hkv, int Sq, int Skv, int D,
  *   o           [B, Hq, D_v] (dtype)
  *   lse         [B, Hq] fp32, or NULL
  *   (D_qk, D_v) (128, 128) with FA_KV_SPLIT, (576, 512) with FA_KV_MLA_SHARED
- *   page_size   >= 1; max_pages_per_seq * page_size >= max_seq_len
+ *   page_size   >= 1; max_pages_per_seq * page_size >= max_seq_len; with
+ *               FA_KV_SPLIT one page (2 * Hkv * page_size * 128 * 2 bytes)
+ *               must be smaller than 2 GiB (FA_ERR_SHAPE otherwise)
  *   max_seq_len host-side upper bound of seq_lens (sizes the grid)
  *   num_splits  0 = let the planner choose; n >= 1 asks for n key splits per
  *               sequence (clamped to what the shape allows)

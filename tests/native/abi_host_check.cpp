@@ -421,6 +421,7 @@ void error_paths() {
   CHECK(dc(1, 32, 8, 128, 128, FA_KV_SPLIT, 16, 3, 64, 8) == FA_ERR_SHAPE, "pages short");
   CHECK(dc(1, 32, 8, 128, 128, FA_KV_SPLIT, 16, 4, 64, 0) == FA_ERR_SHAPE, "no pages");
   CHECK(dc(1, 32, 8, 64, 64, FA_KV_SPLIT, 16, 4, 64, 8) == FA_ERR_UNSUPPORTED, "D=64 decode");
+  CHECK(dc(1, 64, 64, 128, 128, FA_KV_SPLIT, 65536, 1, 64, 8) == FA_ERR_SHAPE, "2 GiB page");
   CHECK(dc(1, 64, 2, 576, 512, FA_KV_MLA_SHARED, 1, 64, 64, 8) == FA_ERR_SHAPE, "MLA Hkv=2");
   CHECK(dc(1, 64, 1, 512, 512, FA_KV_MLA_SHARED, 1, 64, 64, 8) == FA_ERR_UNSUPPORTED, "MLA D");
   CHECK(g_seen.combine == 0, "a refused call launched a combine");

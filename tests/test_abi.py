@@ -185,6 +185,10 @@ def test_decode_validation(fa):
     assert _err(call, ps=0) == -2
     assert _err(call, maxp=3, maxlen=64) == -2  # 3 pages of 16 < 64 tokens
     assert _err(call, npages=0) == -2
+    # A page of the split pool (K and V of every K/V head) must stay below 2 GiB:
+    # 2 * 64 heads * 65536 slots * 256 bytes is exactly 2 GiB.
+    assert _err(call, Hq=64, Hkv=64, ps=65536, maxp=1, maxlen=64) == -2
+    call(Hq=64, Hkv=64, ps=65535, maxp=1, maxlen=64, B=0)  # just below: accepted
     assert _err(call, Dqk=64, Dv=64) == -3
     assert _err(call, layout=fa.FA_KV_MLA_SHARED) == -3  # needs (576, 512)
     assert _err(call, layout=fa.FA_KV_MLA_SHARED, Dqk=576, Dv=512, Hkv=2) == -2
