@@ -137,7 +137,8 @@ def main():
     ap.add_argument("--traffic", action="store_true",
                     help="run only the launches that the HBM-traffic counter runs measure: a "
                          "256 MiB device copy (calibration), the last prefill microbatch "
-                         "(keys [0, 16384)) and the MLA decode, 3 times each")
+                         "(keys [0, 16384)), the MLA decode and the small-batch GQA decode, "
+                         "3 times each")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the multi-GPU sharding "
@@ -281,6 +282,8 @@ def main():
                              fa.FA_BF16, fa.FA_BF16, ws3, ws3_bytes, stream=sid)
             flush_sum = flush.sum()
             decode_pass()
+            flush_sum = flush.sum()
+            decode_gqa_pass()
         torch.cuda.synchronize()
         eprint("traffic launches done (copy 268435456 B read + written per launch)")
         return
@@ -359,8 +362,10 @@ def main():
 
     sha_pf = source_sha("prefill_kernel.h", "prefill.hip", "combine.hip", "fa_device.h")
     sha_dec = source_sha("decode_mla.hip", "combine.hip", "fa_device.h")
+    sha_gqa = source_sha("decode.hip", "combine.hip", "fa_device.h")
     tr_pf, tr_pf_launch = traffic_for("prefill", sha_pf) or (None, None)
     tr_dec, tr_dec_launch = traffic_for("decode_mla", sha_dec) or (None, None)
+    tr_gqa, tr_gqa_launch = traffic_for("decode_gqa", sha_gqa) or (None, None)
 
     result = {
         "metric": METRIC,
@@ -456,7 +461,8 @@ def main():
             "peak": PEAK_HBM_GBS,
             "unit": "GB/s",
             "frac": round(d5s_gbs / PEAK_HBM_GBS, 4),
-            "traffic": None,
+            "traffic": tr_gqa,
+            "traffic_launch": tr_gqa_launch,
             "kernel": "fa_decode_paged call (GQA decode kernel + split combine)",
         },
     }
