@@ -111,6 +111,34 @@ def test_gqa_decode_page_permutation_bit_exact(fa):
     np.testing.assert_array_equal(l1, l2)
 
 
+@pytest.mark.parametrize("page_size", [16, 5])
+def test_gqa_decode_pool_beyond_4gib(fa, page_size):
+    """Page offsets past 4 GiB: the sequences' pages sit at the top of a pool of
+    about 4.6 GB (8 K/V heads; pages of 64 KB at page size 16), so a row's byte
+    offset needs more than 32 bits. The oracle reads the same pages from a
+    compact host copy."""
+    import torch
+    lens = [300, 700]
+    inp = fi.split_decode_inputs(46, 2, 32, 8, 128, lens, page_size, spare_pages=0)
+    n_used = inp.pool.shape[0]
+    page_bytes = inp.pool[0].nbytes
+    n_total = (4 << 30) // page_bytes + 4096  # the top pages start past 4 GiB
+    base = n_total - n_used
+    log(f"pool of {n_total} pages x {page_bytes} B = {n_total * page_bytes / 1e9:.2f} GB, "
+        f"used pages from {base}")
+    big = torch.empty((n_total,) + inp.pool.shape[1:], dtype=torch.bfloat16, device="cuda")
+    big[base:] = to_dev(inp.pool, "bf16")
+    pt = np.where(inp.page_table >= 0, inp.page_table + base, -1).astype(np.int32)
+    o, lse = fa.decode_paged(to_dev(inp.q, "bf16"), big, i32_dev(pt), i32_dev(inp.seq_lens),
+                             layout=fa.FA_KV_SPLIT, scale=inp.scale, max_seq_len=inp.max_seq_len,
+                             page_size=page_size, return_lse=True)
+    torch.cuda.synchronize()
+    del big
+    ref, ref_lse = oracle.decode_paged(inp)
+    assert_parity(to_f64(o), ref, "bf16", f"pool beyond 4 GiB, page {page_size}")
+    assert_lse(to_f64(lse), ref_lse, "pool beyond 4 GiB")
+
+
 def test_gqa_decode_full_size(fa):
     """Workload 5 in full: batch 4, 32 query / 8 K/V heads, lengths U[1024, 32768],
     page_size 16, NaN in every unused slot; planner-chosen split count."""
@@ -230,6 +258,30 @@ def test_mla_decode_multi_token(fa, heads, Sq, Hq, splits, monkeypatch):
     o, lse = check(fa, inp, f"mla multi Sq={Sq} Hq={Hq}", num_splits=splits)
     if Sq > 2:
         assert np.all(o[1, :Sq - 2] == 0) and np.all(np.isneginf(lse[1, :, :Sq - 2]))
+
+
+@pytest.mark.parametrize("heads", ["32", "64"])
+def test_mla_decode_pool_beyond_4gib(fa, heads, monkeypatch):
+    """MLA rows past 4 GiB: the sequences' pages sit at the top of a pool of
+    about 4.3 GB (1152-byte rows, page size 1); the oracle reads the same rows
+    from a compact host copy."""
+    import torch
+    monkeypatch.setenv("FA_MLA_HEADS", heads)
+    inp = fi.mla_decode_inputs(47, 2, 64, 384)
+    n_used = inp.pool.shape[0]
+    n_total = (4 << 30) // inp.pool[0].nbytes + 4096
+    base = n_total - n_used
+    log(f"MLA pool of {n_total} rows, used rows from {base}, {heads} heads per workgroup")
+    big = torch.empty((n_total,) + inp.pool.shape[1:], dtype=torch.bfloat16, device="cuda")
+    big[base:] = to_dev(inp.pool, "bf16")
+    o, lse = fa.decode_paged(to_dev(inp.q, "bf16"), big, i32_dev(inp.page_table + base),
+                             i32_dev(inp.seq_lens), layout=fa.FA_KV_MLA_SHARED, scale=inp.scale,
+                             max_seq_len=inp.max_seq_len, page_size=1, return_lse=True)
+    torch.cuda.synchronize()
+    del big
+    ref, ref_lse = oracle.decode_paged(inp)
+    assert_parity(to_f64(o), ref, "bf16", f"MLA pool beyond 4 GiB ({heads} heads)")
+    assert_lse(to_f64(lse), ref_lse, "MLA pool beyond 4 GiB")
 
 
 def test_mla_decode_fp16_and_empty(fa):
