@@ -194,7 +194,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   f32x16 oacc[D / 32];
 #pragma unroll
   for (int db = 0; db < D / 32; ++db) oacc[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // The row sum is kept as four partial sums (dot product r of a step feeds
+  // sum r % 4), so accumulating dot products that issue close together are
+  // independent and need no wait states between them.
+  float m_run = -INFINITY, l_run[4] = {0.f, 0.f, 0.f, 0.f};
   // With a mask the scores are already scaled (natural-log domain).
   const float sl2 = AMASK ? 1.4426950408889634f : p.scale_log2;
 
@@ -332,7 +335,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     if (__ballot(grow)) {
       const float m_new = grow ? mx : m_run;
       const float alpha = m_run == -INFINITY ? 0.f : fast_exp2((m_run - m_new) * sl2);
-      l_run *= alpha;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) l_run[i] *= alpha;
 #pragma unroll
       for (int db = 0; db < D / 32; ++db) oacc[db] *= alpha;
       m_run = m_new;
@@ -350,9 +354,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   //     E: for each 8 of tile t's 32 probabilities per lane, 8 (fma, exp2)
   //        pairs and 4 packs to 16 bits (done before the first P V MFMA that
   //        reads them);
-  //     R: the 16 row-sum dot products over the packed probabilities;
-  //     M: the row max of S(t+1), two chains of max3 (they start once the
+  //     R: the 16 row-sum dot products over the packed probabilities, into
+  //        four partial sums;
+  //     M: the row max of S(t+1), four chains of max3 (they start once the
   //        score MFMAs have drained; returned in mx_next).
+  //   (Accumulating ops of one chain that issue within two instructions of
+  //   each other need a wait state between them; four chains avoid it.)
   //   Spread over both halves of the step the vector work stays near four ops
   //   per MFMA, which the SIMD co-issues with the matrix core; packed under
   //   the score MFMAs alone it was six, and the vector unit set the pace.
@@ -380,7 +387,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     static_assert((NE + NR) / VPS >= NQK + (AHEAD ? 0 : 2), "row max before the scores drain");
     float pv[32];
     u32x4 pb[4];
-    float mxa = -INFINITY, mxb = -INFINITY;
+    // Four independent max chains (unit u feeds chain u % 4).
+    float mxc[4] = {-INFINITY, -INFINITY, -INFINITY, -INFINITY};
     auto pin = [](float& x) { asm volatile("" : "+v"(x)); };
     // Masked score of S(t+1) element (kb, i): scale s + M (natural-log domain).
     auto masked = [&](int kb, int i) {
@@ -411,12 +419,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
         }
       } else if constexpr (k < NE + NR) {
         constexpr int r = k - NE;
-        l_run = T::sum2(pb[r >> 2][r & 3], l_run);
-        pin(l_run);
+        l_run[r & 3] = T::sum2(pb[r >> 2][r & 3], l_run[r & 3]);
+        pin(l_run[r & 3]);
       } else {
         constexpr int u = (k - NE - NR) / MW, sub = (k - NE - NR) % MW;
         constexpr int kb = u & 1, i = 2 * (u >> 1);
-        float& m = kb ? mxb : mxa;
+        float& m = mxc[u & 3];
         if constexpr (AHEAD) {
           if constexpr (sub == 0 || sub == 2) {
             float x = masked(kb, i + sub / 2);
@@ -476,7 +484,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       });
     });
     __builtin_amdgcn_sched_barrier(0);
-    mx_next = max_xor32(fmaxf(mxa, mxb));
+    mx_next = max_xor32(fmaxf(fmaxf(mxc[0], mxc[1]), fmaxf(mxc[2], mxc[3])));
   };
 
   // Tiles [t_begin, t_mask) are visible to every row of the workgroup and lie
@@ -577,7 +585,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   if (t < t_end) step(kMasked, t, sA, sB);
 
   // Epilogue: both lane halves hold parts of the row sum.
-  const float l_tot = sum_xor32(l_run);
+  const float l_tot = sum_xor32((l_run[0] + l_run[1]) + (l_run[2] + l_run[3]));
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   // (With a mask m_run is already scaled.)
   const float lse = l_tot > 0.f ? (AMASK ? m_run : m_run * p.scale) + __logf(l_tot) : -INFINITY;
