@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
   //   Masked scores are -inf already, and exp2(-inf * sl2 + nb) = 0 because
   //   sl2 > 0 (a zero scale is passed as the smallest positive one).
   auto body = [&](f32x16 (&cur)[2], f32x16 (&nxt)[2], const char* Ks, const char* Vs, float nb,
-                  float& mx_next, auto ahead_tag, const char* mnext) {
+                  float& mx_next, auto ahead_tag, const char* mnext, auto&& copy_k, auto&& copy_v) {
     // ahead: add the additive mask of tile t + 1 (read from LDS at mnext) to
     // S(t+1) in the M part, under the P V MFMAs, instead of at the next step's
     // start: each M unit is then two (unpack, fma) pairs and a max3.
@@ -379,6 +379,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     constexpr int NE = 4 * 20, NR = 16, NM = 16 * MW;
     constexpr int NOPS = NE + NR + NM;
     constexpr int NSLOT = NQK + NPV;
+    // Head size 128: the step's K and V copies go out under the score MFMAs
+    // of slots CPK and CPV instead of in one burst before the block (workload
+    // 3 -0.3 to -0.9%, masked -0.6 to -1.5%, two boxes); head size 64 keeps the
+    // burst (its block is half as long).
+    constexpr int CPK = D == 128 ? 2 : -1, CPV = D == 128 ? 6 : -1;
     constexpr int VPS = (NOPS + NSLOT - 1) / NSLOT;
     // E(jj) ends before the first P V MFMA of jj; M starts after the last
     // score MFMA (two slots after it when that costs no extra slot).
@@ -451,11 +456,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
       va[i] = lds_read_tr16(Vs + voffA + 2048 * C::NCB * jj + 512 * db);
       vb[i] = lds_read_tr16(Vs + voffB + 2048 * C::NCB * jj + 512 * db);
     };
+    if constexpr (CPK < 0) copy_k();
+    if constexpr (CPV < 0) copy_v();
 #pragma unroll
     for (int i = 0; i < PD; ++i) kread(i);
     static_for<0, NSLOT>([&](auto ic) {
       constexpr int i = decltype(ic)::value;
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (i == CPK) copy_k();
+      if constexpr (i == CPV) copy_v();
       if constexpr (i < NQK) {
         if constexpr (i + PD < NQK) kread(i + PD);
         else vread(i + PD - NQK);
@@ -541,8 +550,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     lds_barrier();
     constexpr bool ahead = AM == 2;
     if constexpr (AMASK && !ahead) read_mask(t);
-    if (t + 2 < t_end) issue_k(t + 2);
-    if (t + 1 < t_end) issue_v(t + 1);
+    auto copy_k = [&] {
+      if (t + 2 < t_end) issue_k(t + 2);
+    };
+    auto copy_v = [&] {
+      if (t + 1 < t_end) issue_v(t + 1);
+    };
     if constexpr (AMASK) {
       if constexpr (ahead) {
         if (t + 2 < t_end) issue_mask(t + 2);
@@ -560,9 +573,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_kernel(PrefillParams p) {
     const float nb = rescale(mx);
     if constexpr (ahead)
       body(cur, nxt, smem + k_stage(t + 1), smem + v_stage(t), nb, mx_pend, kAhead,
-           mread + m_stage(t + 1));
+           mread + m_stage(t + 1), copy_k, copy_v);
     else
-      body(cur, nxt, smem + k_stage(t + 1), smem + v_stage(t), nb, mx_pend, kNow, nullptr);
+      body(cur, nxt, smem + k_stage(t + 1), smem + v_stage(t), nb, mx_pend, kNow, nullptr, copy_k,
+           copy_v);
     debug_step_barrier();
   };
   constexpr std::integral_constant<bool, false> kFull{};

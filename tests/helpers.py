@@ -49,13 +49,31 @@ def metrics(out: np.ndarray, ref: np.ndarray) -> dict:
     }
 
 
-def assert_parity(out, ref, in_dtype: str, what: str = "") -> dict:
+# Relative half-ulp of a 16-bit type (round to nearest).
+HALF_ULP = {"bf16": 2.0 ** -8, "fp16": 2.0 ** -11}
+
+
+def assert_parity(out, ref, in_dtype: str, what: str = "", partial_dtype: str = None) -> dict:
+    """partial_dtype: the 16-bit type of key-split partial outputs, when the
+    result went through them. Each partial row is rounded to that type before
+    the combine, and the output rounds the combined value again, so each
+    element may also be off by half an ulp of its own magnitude: the max-abs
+    gate becomes |o - ref| <= max_abs + half_ulp * |ref| per element. (Only a
+    peaked softmax, where an output row is nearly one value row with |O| up to
+    ~4.6, makes that term matter: one bf16 ulp is 0.031 in [4, 8).)"""
     m = metrics(out, ref)
     mx, mean = TOL[in_dtype]
     log(f"parity {what}: " + " ".join(f"{k}={v:.3g}" if isinstance(v, float) else f"{k}={v}"
                                       for k, v in m.items()))
     assert m["finite"], f"{what}: non-finite output"
-    assert m["max_abs"] <= mx, f"{what}: max-abs {m['max_abs']:.3g} > {mx}"
+    if partial_dtype in HALF_ULP:
+        o = np.asarray(out, dtype=np.float64).ravel()
+        r = np.asarray(ref, dtype=np.float64).ravel()
+        excess = np.abs(o - r) - (mx + HALF_ULP[partial_dtype] * np.abs(r))
+        assert excess.size == 0 or excess.max() <= 0, \
+            f"{what}: max-abs {m['max_abs']:.3g} beyond {mx} + half an ulp of the partials"
+    else:
+        assert m["max_abs"] <= mx, f"{what}: max-abs {m['max_abs']:.3g} > {mx}"
     assert m["mean_abs"] <= mean, f"{what}: mean-abs {m['mean_abs']:.3g} > {mean}"
     if np.linalg.norm(np.asarray(ref)) > 0:
         assert m["rel_rms"] <= 1e-2, f"{what}: relative RMS {m['rel_rms']:.3g} > 1e-2"

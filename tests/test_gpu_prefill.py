@@ -137,6 +137,36 @@ def test_prefill_pingpong(fa, shape, splits, monkeypatch):
     assert_lse(to_f64(lse), ref_lse, f"ping-pong splits={splits} {shape}")
 
 
+SCALES = [None, -0.07, 0.0, 0.69, 1.0, -2.0]  # None: 1/sqrt(D)
+SCALE_SHAPES = [
+    (1, 4, 2, 200, 333, 64, True, "bf16", "bf16"),
+    (1, 4, 2, 333, 900, 128, True, "bf16", "bf16"),
+    (1, 8, 2, 77, 300, 128, False, "fp16", "fp16"),
+    (1, 2, 2, 129, 129, 64, True, "fp16", "fp32"),
+]
+
+
+@pytest.mark.parametrize("splits", ["1", "3"])
+@pytest.mark.parametrize("scale", SCALES, ids=lambda s: f"scale={s}")
+@pytest.mark.parametrize("shape", SCALE_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_prefill_scales(fa, shape, scale, splits, monkeypatch):
+    """The unmasked kernel over negative, zero and large scales (a large scale
+    makes the softmax peaked, where the rounding of each score matters most),
+    with and without key splits. With splits and a 16-bit output the partial
+    rows are 16-bit too, and the gate allows their one extra rounding."""
+    B, Hq, Hkv, Sq, Skv, D, causal, it, ot = shape
+    monkeypatch.setenv("FA_PREFILL_SPLITS", splits)
+    inp = fi.prefill_inputs(24, B, Hq, Hkv, Sq, Skv, D, causal, it, ot)
+    if scale is not None:
+        inp.scale = fi.f32(scale)
+    what = f"scale={inp.scale} splits={splits} {shape}"
+    log(f"prefill {what}")
+    o, lse = run(fa, inp)
+    ref, ref_lse = oracle.prefill(inp)
+    assert_parity(to_f64(o), ref, it, what, partial_dtype=ot if splits != "1" else None)
+    assert_lse(to_f64(lse), ref_lse, what, dtype=it)
+
+
 def test_prefill_no_keys(fa):
     import torch
     q = torch.randn(1, 40, 2, 64, device="cuda").to(torch.bfloat16)
