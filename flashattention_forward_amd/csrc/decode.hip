@@ -33,26 +33,28 @@ namespace fa {
 // ---------------------------------------------------------------------------
 // Grouped-query decode over the split K/V pool [P, 2, Hkv, page, 128].
 // One wave is one work unit (sequence b, K/V head g, block of up to 16 query
-// heads of the group, key split); a workgroup holds 4 independent units.
+// heads of the group, key split); a workgroup holds 8 independent units.
 // ---------------------------------------------------------------------------
 constexpr int DS_D = 128;
 constexpr int DS_VS = DS_D + 16;  // V row stride in LDS (elements)
 
 template <typename TI, int PS>
-__global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) {
+__global__ __launch_bounds__(512) void decode_split_kernel(DecodeSplitParams p) {
   using T = in_traits<TI>;
   constexpr int D = DS_D;
-  __shared__ __attribute__((aligned(16))) char smem[4][DEC_TILE * DS_VS * 2];
+  __shared__ __attribute__((aligned(16))) char smem[8][DEC_TILE * DS_VS * 2];
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  int unit = blockIdx.x * 4 + w;
+  int unit = blockIdx.x * 8 + w;
   if (unit >= p.n_units) return;  // whole wave leaves; the kernel has no barriers
   char* vlds = smem[w];
 
   // Units are numbered with the K/V head fastest: the waves of a workgroup take
   // neighbouring head slices of the same pages (the same key range of one
-  // sequence), and the units of a split past its sequence's end fill whole
-  // workgroups that leave at once (workload 5 48.0 -> 47.0 us against
-  // split-fastest numbering).
+  // sequence; with 8 K/V heads the 8 waves read each 16-token page of K and V
+  // whole, 2 x 32 KB contiguous, at about the same time), and the units of a
+  // split past its sequence's end fill whole workgroups that leave at once.
+  // Workload 5: 48.0 us with split-fastest numbering in 4-wave workgroups,
+  // 47.0 with head-fastest, 45.2 with 8-wave workgroups (one process each).
   const int S = p.n_splits;
   const int g = unit % p.Hkv;
   unit /= p.Hkv;
@@ -283,13 +285,13 @@ __global__ __launch_bounds__(256) void decode_split_kernel(DecodeSplitParams p) 
 
 template <typename TI>
 static hipError_t split_dispatch(const DecodeSplitParams& p, hipStream_t stream) {
-  const int blocks = (p.n_units + 3) / 4;
+  const int blocks = (p.n_units + 7) / 8;
   if (p.page_size == 16)
-    hipLaunchKernelGGL((decode_split_kernel<TI, 16>), dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<TI, 16>), dim3(blocks), dim3(512), 0, stream, p);
   else if (p.page_size == 1)
-    hipLaunchKernelGGL((decode_split_kernel<TI, 1>), dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<TI, 1>), dim3(blocks), dim3(512), 0, stream, p);
   else
-    hipLaunchKernelGGL((decode_split_kernel<TI, 0>), dim3(blocks), dim3(256), 0, stream, p);
+    hipLaunchKernelGGL((decode_split_kernel<TI, 0>), dim3(blocks), dim3(512), 0, stream, p);
   return hipGetLastError();
 }
 
