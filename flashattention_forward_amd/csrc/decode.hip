@@ -43,7 +43,8 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeSplitParams p) 
   using T = in_traits<TI>;
   constexpr int D = DS_D;
   __shared__ __attribute__((aligned(16))) char smem[8][DEC_TILE * DS_VS * 2];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // unit indices stay scalar
   int unit = blockIdx.x * 8 + w;
   if (unit >= p.n_units) return;  // whole wave leaves; the kernel has no barriers
   char* vlds = smem[w];
@@ -95,15 +96,18 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeSplitParams p) 
   // half of a tile lies in one page, so a lane needs the page ids of the two
   // halves only (HALVES); otherwise it needs one per row. The ids are fetched
   // two tiles ahead, so no row load waits on a page-table load; the table is
-  // read at a clamped (valid) index and the id replaced by -1 past the split's
-  // end, with no branch. Invalid rows (past the split, or with an out-of-range
-  // page id) load the pool's first row and are zeroed by a select. Key and
+  // read at keys clamped to max_seq_len - 1 (inside the table, whose rows cover
+  // max_seq_len tokens), so the first fetch does not wait for the sequence's
+  // length: the length, the first page ids and the queries are three loads in
+  // flight together, and the first rows follow one round trip later. Invalid
+  // rows (past the split, or with an out-of-range page id) load the pool's
+  // first row and are zeroed by a select. Key and
   // slot arithmetic is unsigned (keys are never negative), and a page's bytes
   // fit in 32 bits (checked on the host), so a row's offset is one 32 x 32 ->
   // 64-bit multiply-add.
   constexpr bool HALVES = PS > 0 && PS % 16 == 0;
   constexpr int NPG = HALVES ? 2 : 10;
-  const unsigned last_key = (unsigned)max(t1 - 1, 0);
+  const unsigned last_key = (unsigned)max(p.max_seq_len - 1, 0);
   const unsigned psize = PS > 0 ? (unsigned)PS : (unsigned)p.page_size;
   auto row_key = [&](int r, int tt) { return tt + (r < 2 ? 16 * r + c16 : gq + 4 * (r - 2)); };
   auto fetch_pages = [&](int (&pg)[NPG], int tt) {
@@ -111,8 +115,7 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeSplitParams p) 
     for (int i = 0; i < NPG; ++i) {
       const int key = HALVES ? tt + 16 * i : row_key(i, tt);
       const unsigned kc = min((unsigned)key, last_key);
-      const int id = ptab[kc / psize];
-      pg[i] = key < t1 ? id : -1;
+      pg[i] = ptab[kc / psize];  // (row_off rejects keys past the split)
     }
   };
   auto row_off = [&](const int (&pg)[NPG], int r, int tt, bool& ok) -> uint64_t {
@@ -171,8 +174,8 @@ __global__ __launch_bounds__(512) void decode_split_kernel(DecodeSplitParams p) 
 
   // pg holds the page ids of the tile whose loads are issued next.
   int pg[NPG];
+  fetch_pages(pg, t0);
   if (t0 < t1) {
-    fetch_pages(pg, t0);
     load_k(pg, t0);
     load_v(pg, t0);
     fetch_pages(pg, t0 + DEC_TILE);
