@@ -186,13 +186,14 @@ DecodePlan plan_decode(int B, int Hq, int Hkv, int D_v, int max_seq_len, fa_kv_l
     pl.n_hblk = ceil_div((Hq / Hkv) * Sq, 16);  // rows: new tokens x heads of a group
     units = (int64_t)B * Hkv * pl.n_hblk;  // one wave per unit
     // 16 waves per CU, twice the 8 that are resident at a time (the kernel's
-    // 180 VGPRs + 36 AGPRs leave room for two waves per SIMD): in a ragged
-    // batch the splits past a shorter sequence's end (about half of them for
-    // lengths uniform up to max_seq_len) exit at once without holding a slot,
-    // and a wave keeps one tile in flight, so shorter chains of tiles pay.
-    // Measured on 4 sequences of 1.8K-23K tokens, 32/8 heads: 92 splits of 256
-    // tokens take 50 us against 59 us for 62 of 384 (a grid sized to the
-    // resident waves).
+    // 168 VGPRs leave room for two waves per SIMD, one 8-wave workgroup per
+    // CU): in a ragged batch the splits past a shorter sequence's end (about
+    // half of them for lengths uniform up to max_seq_len) exit at once without
+    // holding a slot, and a wave keeps one tile in flight, so shorter chains of
+    // tiles pay. Measured on 4 sequences of 1.8K-23K tokens, 32/8 heads: 92
+    // splits of 256 tokens take 50 us against 59 us for 62 of 384 (a grid
+    // sized to the resident waves); with 8-wave workgroups 64 / 80 / 92 / 105
+    // / 128 / 184 splits took 51.3 / 48.2 / 44.6 / 44.6 / 45.2 / 51.5 us.
     target = 16 * (int64_t)planner_cus();
   }
   int S = 1;
