@@ -61,6 +61,18 @@ def test_gqa_decode_small(fa, page_size, G):
     check(fa, inp, f"gqa page={page_size} G={G}")
 
 
+@pytest.mark.parametrize("splits", [1, 5, 0])
+@pytest.mark.parametrize("Hkv,G,page_size", [(3, 2, 16), (5, 4, 5), (7, 1, 16)])
+def test_gqa_decode_odd_kv_heads(fa, Hkv, G, page_size, splits):
+    """K/V head counts that do not divide a workgroup's 8 waves: a workgroup
+    then holds units of several key ranges and sequences (units are numbered
+    with the K/V head fastest), and the last one is partly empty."""
+    lens = [777, 1, 1500, 96, 0]
+    inp = fi.split_decode_inputs(48 + Hkv, 5, G * Hkv, Hkv, 128, lens, page_size)
+    log(f"gqa decode Hkv={Hkv} G={G} page={page_size} splits={splits}")
+    check(fa, inp, f"gqa Hkv={Hkv} G={G} page={page_size} splits={splits}", num_splits=splits)
+
+
 @pytest.mark.parametrize("splits", [1, 2, 3, 8, 24, 0])
 def test_gqa_decode_split_sweep(fa, splits):
     inp = fi.split_decode_inputs(40, 3, 8, 2, 128, [1500, 700, 64], 16)
