@@ -39,7 +39,7 @@ def declared_params(name):
     return [re.findall(r"(\w+)\s*$", p.strip())[0] for p in m.group(1).split(",")]
 
 
-def test_north_star_argument_order():
+def test_specified_argument_order():
     """The two calls the path is specified by keep their argument lists:
     fa_prefill(q,k,v,o,B,Hq,Hkv,Sq,Skv,D,causal,scale,stream) exactly, and
     fa_decode_paged(q,kv_pool,page_table,seq_lens,...,stream)."""
